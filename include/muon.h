@@ -1,0 +1,149 @@
+/*
+ * muon.h -- C ABI of the MI355X (gfx950) Muon optimizer-step library.
+ *
+ * The operation (sources: Keller Jordan's "new optimizer" X thread,
+ * xunroll.com/thread/1842300916864844014, tweets 2/8, 5/8 and 6/8; the
+ * momentum convention from "07. Training neural networks", section
+ * "Momentum"):
+ *
+ *   for every 2-D parameter matrix W (rows x cols, fp32) with gradient G and
+ *   momentum buffer M:
+ *     M  <- beta * M + G                      SGD momentum buffer
+ *     U  <- G + beta * M                      Nesterov look-ahead
+ *     X0 <- bf16( U / (||U||_F + 1e-7) )      transposed first if rows > cols
+ *     repeat ns_steps times (quintic Newton-Schulz, in bfloat16):
+ *        A <- bf16(X X^T);  B <- bf16(b A + c A A);  X <- bf16(a X + B X)
+ *     W  <- W - lr * X                        (X transposed back)
+ *
+ * The thread states the design: orthogonalise each parameter's update after
+ * Nesterov momentum, with a quintic Newton-Schulz iteration run in bfloat16,
+ * whose coefficients maximise the slope at zero at the cost of exact
+ * convergence.  The normalisation, the epsilon, the coefficient values and the
+ * bf16 storage points are readings of those statements, not quotes: every
+ * product accumulates in fp32 from bf16 operands; A, B and each new X are
+ * rounded to bf16 (round to nearest even); the epilogue combinations
+ * b*A + c*(AA) and a*X + (BX) are two fp32 products and one fp32 sum, not
+ * fused.  No weight decay (the thread's replies report it as worse).  Only
+ * 2-D matrices belong here; 1-D parameters go to another optimizer.
+ *
+ * Conventions for every entry point:
+ *   - All matrix pointers are device pointers (HIP device memory, e.g. from
+ *     PyTorch), row-major, contiguous, 4-byte aligned, caller-owned, and do
+ *     not alias one another.  Arrays of pointers and shapes are host arrays,
+ *     read only during the call.
+ *   - Work is enqueued on `stream` and the call returns without waiting.
+ *     Kernel faults surface at the caller's next synchronisation.  Calls that
+ *     overlap in time on one device must use the same stream (they share the
+ *     library's workspace).
+ *   - Arguments are validated on the host before any HIP call; on failure
+ *     the call returns a negative code, enqueues nothing and
+ *     muon_last_error() describes the problem.
+ *   - Return codes: MUON_OK (0), MUON_EINVAL (bad argument), MUON_ENOMEM
+ *     (workspace allocation failed or caller workspace too small),
+ *     MUON_EHIP (a HIP runtime call or launch failed; the HIP error string is
+ *     in muon_last_error()).
+ */
+#ifndef MUON_H_
+#define MUON_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MUON_OK 0
+#define MUON_EINVAL (-1)
+#define MUON_ENOMEM (-2)
+#define MUON_EHIP (-3)
+
+/* Largest accepted ns_steps and matrix count per call. */
+#define MUON_MAX_NS_STEPS 64
+#define MUON_MAX_MATRICES 65536
+
+/* Matrix shape in the caller's orientation. */
+typedef struct {
+  int64_t rows;
+  int64_t cols;
+} muon_shape_t;
+
+/*
+ * One Muon step over n independent matrices.
+ *   params[i]   fp32 rows x cols, updated in place
+ *   grads[i]    fp32 rows x cols, read only
+ *   momentum[i] fp32 rows x cols, updated in place (zero before the first step)
+ *   shapes[i]   rows, cols >= 1; rows * cols < 2^31
+ *   lr          finite
+ *   beta        in [0, 1)
+ *   ns_steps    0 .. MUON_MAX_NS_STEPS (0 applies the normalised bf16 X0)
+ *   coeffs      host array {a, b, c}, finite; the same triple every iteration
+ * n == 0 is a no-op.  A zero gradient with a zero buffer leaves W unchanged.
+ * NaN/Inf in the inputs propagate; nothing checks for them.
+ */
+int muon_step(float* const* params, const float* const* grads, float* const* momentum,
+              const muon_shape_t* shapes, int n, float lr, float beta, int ns_steps,
+              const float* coeffs, hipStream_t stream);
+
+/*
+ * Same as muon_step, and additionally writes the bf16 update X (the value
+ * applied as W -= lr * X) to updates[i] (uint16 bf16 bit patterns,
+ * rows x cols, caller orientation).  updates may be NULL, or any element may
+ * be NULL, to skip that output.
+ */
+int muon_step_ex(float* const* params, const float* const* grads, float* const* momentum,
+                 const muon_shape_t* shapes, int n, float lr, float beta, int ns_steps,
+                 const float* coeffs, uint16_t* const* updates, hipStream_t stream);
+
+/*
+ * The Newton-Schulz core alone: out[i] = iterate(x[i]) with the same
+ * storage points as muon_step, no normalisation, no momentum.  x[i] and out[i]
+ * are bf16 bit patterns (uint16), rows x cols in the caller's orientation
+ * (tall matrices are transposed internally); out may equal x.  ns_steps = 0
+ * copies.
+ */
+int muon_newton_schulz(const uint16_t* const* x, uint16_t* const* out, const muon_shape_t* shapes,
+                       int n, int ns_steps, const float* coeffs, hipStream_t stream);
+
+/* Thread-local description of the last failing call on this thread ("" if none). */
+const char* muon_last_error(void);
+
+/*
+ * Device workspace bytes a call over these shapes needs (bf16 iterates,
+ * Gram and polynomial matrices, norm partials, work lists).  Pure host
+ * computation.  Returns 0 and sets the error text for invalid shapes.
+ */
+size_t muon_workspace_bytes(const muon_shape_t* shapes, int n);
+
+/*
+ * Hand the library a caller-owned device workspace for the current device
+ * (NULL/0 returns to library-owned workspace).  The caller keeps it alive
+ * until muon_release() or another muon_set_workspace() call; calls that need
+ * more than `bytes` fail with MUON_ENOMEM.
+ */
+int muon_set_workspace(void* dev_ptr, size_t bytes);
+
+/* Free the library's cached workspace and plans on all devices (synchronises). */
+void muon_release(void);
+
+/*
+ * Kernel timing for measurement.  muon_timing_enable(k) brackets every
+ * subsequent launch of kernel family k with HIP events on the launch stream;
+ * k = -1 stops.  muon_timing_read waits for the recorded events and returns
+ * the summed kernel time and the number of launches since the last read.
+ */
+#define MUON_KERNEL_MOMENTUM 0 /* momentum update + norm partial sums */
+#define MUON_KERNEL_CAST 1     /* normalise + transpose + cast to bf16 */
+#define MUON_KERNEL_GRAM 2     /* A = X X^T */
+#define MUON_KERNEL_POLY 3     /* B = b A + c A A */
+#define MUON_KERNEL_UPDATE 4   /* X <- a X + B X */
+#define MUON_KERNEL_APPLY 5    /* W -= lr X */
+int muon_timing_enable(int kernel);
+int muon_timing_read(double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MUON_H_ */

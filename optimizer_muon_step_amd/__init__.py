@@ -1,0 +1,151 @@
+"""Muon optimizer step on MI355X: Python binding of libmuon.so.
+
+Thin argument marshalling over the C ABI declared in include/muon.h; every
+step of the computation runs in the library's HIP kernels.  Tensors are torch
+tensors on the current HIP device: fp32 params/grads/momentum, bf16 for the
+Newton-Schulz entry.  Calls enqueue on torch's current stream (or `stream`)
+and return without synchronising.
+"""
+from __future__ import annotations
+
+import ctypes
+
+from . import _lib
+
+__all__ = [
+    "DEFAULT_COEFFS", "MuonError", "muon_step", "muon_newton_schulz", "muon_workspace_bytes",
+    "muon_set_workspace", "muon_release", "muon_timing_enable", "muon_timing_read", "muon_last_error",
+    "KERNEL_MOMENTUM", "KERNEL_CAST", "KERNEL_GRAM", "KERNEL_POLY", "KERNEL_UPDATE", "KERNEL_APPLY",
+]
+
+DEFAULT_COEFFS = (3.4445, -4.7750, 2.0315)
+KERNEL_MOMENTUM, KERNEL_CAST, KERNEL_GRAM, KERNEL_POLY, KERNEL_UPDATE, KERNEL_APPLY = range(6)
+_CODES = {-1: "MUON_EINVAL", -2: "MUON_ENOMEM", -3: "MUON_EHIP"}
+
+
+class MuonError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{_CODES.get(code, code)}: {msg}")
+        self.code = code
+
+
+def muon_last_error() -> str:
+    return (_lib.load().muon_last_error() or b"").decode()
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        raise MuonError(rc, muon_last_error())
+
+
+def _stream_handle(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _fp32_matrix(t, what):
+    import torch
+    if not isinstance(t, torch.Tensor) or t.dim() != 2:
+        raise ValueError(f"{what}: expected a 2-D tensor (1-D parameters belong to another optimizer)")
+    if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{what}: expected a contiguous float32 tensor on the GPU")
+    return t.data_ptr()
+
+
+def _bf16_matrix(t, what):
+    import torch
+    if not isinstance(t, torch.Tensor) or t.dim() != 2:
+        raise ValueError(f"{what}: expected a 2-D tensor")
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16) or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{what}: expected a contiguous bfloat16 tensor on the GPU")
+    return t.data_ptr()
+
+
+def muon_step(params, grads, momentum, lr=0.02, beta=0.95, ns_steps=5, coeffs=DEFAULT_COEFFS,
+              updates=None, stream=None) -> None:
+    """One Muon step over lists of 2-D fp32 tensors (params and momentum updated in place).
+    `updates`, if given, is a list of bf16 tensors (or None entries) receiving the applied update."""
+    n = len(params)
+    if len(grads) != n or len(momentum) != n:
+        raise ValueError("params, grads and momentum must have the same length")
+    shapes = []
+    for i, (p, g, m) in enumerate(zip(params, grads, momentum)):
+        _fp32_matrix(p, f"params[{i}]"), _fp32_matrix(g, f"grads[{i}]"), _fp32_matrix(m, f"momentum[{i}]")
+        if g.shape != p.shape or m.shape != p.shape:
+            raise ValueError(f"matrix {i}: shapes differ")
+        shapes.append(tuple(p.shape))
+    lib = _lib.load()
+    P = _lib.ptr_array([p.data_ptr() for p in params])
+    G = _lib.ptr_array([g.data_ptr() for g in grads])
+    M = _lib.ptr_array([m.data_ptr() for m in momentum])
+    S = _lib.shape_array(shapes)
+    C = _lib.float3(coeffs)
+    st = ctypes.c_void_p(_stream_handle(stream))
+    if updates is None:
+        rc = lib.muon_step(P, G, M, S, n, float(lr), float(beta), int(ns_steps), C, st)
+    else:
+        if len(updates) != n:
+            raise ValueError("updates must have one entry per matrix")
+        ptrs = []
+        for i, u in enumerate(updates):
+            if u is None:
+                ptrs.append(None)
+                continue
+            _bf16_matrix(u, f"updates[{i}]")
+            if tuple(u.shape) != shapes[i]:
+                raise ValueError(f"updates[{i}]: shape differs from params[{i}]")
+            ptrs.append(u.data_ptr())
+        U = _lib.ptr_array(ptrs)
+        rc = lib.muon_step_ex(P, G, M, S, n, float(lr), float(beta), int(ns_steps), C, U, st)
+    _check(rc)
+
+
+def muon_newton_schulz(xs, outs, ns_steps=5, coeffs=DEFAULT_COEFFS, stream=None) -> None:
+    """The Newton-Schulz core alone on bf16 matrices (no normalisation)."""
+    n = len(xs)
+    if len(outs) != n:
+        raise ValueError("xs and outs must have the same length")
+    shapes = []
+    for i, (x, o) in enumerate(zip(xs, outs)):
+        _bf16_matrix(x, f"xs[{i}]"), _bf16_matrix(o, f"outs[{i}]")
+        if x.shape != o.shape:
+            raise ValueError(f"matrix {i}: shapes differ")
+        shapes.append(tuple(x.shape))
+    lib = _lib.load()
+    rc = lib.muon_newton_schulz(_lib.ptr_array([x.data_ptr() for x in xs]),
+                                _lib.ptr_array([o.data_ptr() for o in outs]),
+                                _lib.shape_array(shapes), n, int(ns_steps), _lib.float3(coeffs),
+                                ctypes.c_void_p(_stream_handle(stream)))
+    _check(rc)
+
+
+def muon_workspace_bytes(shapes) -> int:
+    lib = _lib.load()
+    b = lib.muon_workspace_bytes(_lib.shape_array(shapes), len(shapes))
+    if b == 0 and len(shapes) > 0:
+        raise MuonError(-1, muon_last_error())
+    return int(b)
+
+
+def muon_set_workspace(ptr: int | None, nbytes: int = 0) -> None:
+    _check(_lib.load().muon_set_workspace(ctypes.c_void_p(ptr or 0), int(nbytes)))
+
+
+def muon_release() -> None:
+    _lib.load().muon_release()
+
+
+def muon_timing_enable(kernel: int) -> None:
+    _check(_lib.load().muon_timing_enable(int(kernel)))
+
+
+def muon_timing_read():
+    """(total milliseconds, number of launches) of the timed kernel family since the last read."""
+    ms = ctypes.c_double()
+    cnt = ctypes.c_int64()
+    _check(_lib.load().muon_timing_read(ctypes.byref(ms), ctypes.byref(cnt)))
+    return ms.value, cnt.value

@@ -1,0 +1,554 @@
+// C ABI of the Muon step library: argument checks, the per-call plan (shape
+// canonicalisation, padding, workspace layout, work lists), the per-device
+// workspace and plan cache, and the launch sequence.  The operation itself is
+// described in include/muon.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <list>
+#include <map>
+#include <memory>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/muon.h"
+#include "muon_internal.h"
+
+using namespace muon;
+
+namespace {
+
+thread_local std::string g_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return code;
+}
+
+int fail_hip(hipError_t e, const char* what) {
+  return fail(MUON_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v, size_t a = kAlign) { return (v + a - 1) / a * a; }
+int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+// Control region at the start of every workspace: one completion counter and
+// one scale per matrix slot.  The counters are zeroed when a workspace is
+// acquired and every call leaves them at zero again.
+constexpr size_t kCounterBytes = sizeof(uint32_t) * MUON_MAX_MATRICES;
+constexpr size_t kScaleBytes = sizeof(float) * MUON_MAX_MATRICES;
+constexpr size_t kControlBytes = kCounterBytes + kScaleBytes;
+
+struct Geometry {
+  int32_t rows, cols, m, n, m_pad, n_pad, transposed, part_cnt;
+  size_t x_bytes, a_bytes, part_bytes;
+};
+
+Geometry geometry_of(const muon_shape_t& s) {
+  Geometry g{};
+  g.rows = (int32_t)s.rows;
+  g.cols = (int32_t)s.cols;
+  g.transposed = s.rows > s.cols;
+  g.m = (int32_t)std::min(s.rows, s.cols);
+  g.n = (int32_t)std::max(s.rows, s.cols);
+  g.m_pad = (int32_t)round_up(g.m, NS_TILE);
+  g.n_pad = (int32_t)round_up(g.n, NS_TILE);
+  g.part_cnt = (int32_t)((s.rows * s.cols + MOM_CHUNK - 1) / MOM_CHUNK);
+  g.x_bytes = align_up((size_t)g.m_pad * g.n_pad * 2);
+  g.a_bytes = align_up((size_t)g.m_pad * g.m_pad * 2);
+  g.part_bytes = align_up((size_t)g.part_cnt * sizeof(double));
+  return g;
+}
+
+int check_shapes(const muon_shape_t* shapes, int n) {
+  if (n < 0 || n > MUON_MAX_MATRICES) return fail(MUON_EINVAL, "n = %d outside [0, %d]", n, MUON_MAX_MATRICES);
+  if (n > 0 && !shapes) return fail(MUON_EINVAL, "shapes is NULL");
+  for (int i = 0; i < n; ++i) {
+    const int64_t r = shapes[i].rows, c = shapes[i].cols;
+    if (r < 1 || c < 1) return fail(MUON_EINVAL, "matrix %d: shape %lld x %lld (both must be >= 1)", i, (long long)r, (long long)c);
+    if (r > (int64_t)INT32_MAX || c > (int64_t)INT32_MAX || r * c >= ((int64_t)1 << 31))
+      return fail(MUON_EINVAL, "matrix %d: shape %lld x %lld has 2^31 or more elements", i, (long long)r, (long long)c);
+    const Geometry g = geometry_of(shapes[i]);
+    if ((int64_t)g.m_pad * g.n_pad >= ((int64_t)1 << 31))
+      return fail(MUON_EINVAL, "matrix %d: padded shape too large", i);
+  }
+  return MUON_OK;
+}
+
+size_t workspace_bytes_of(const muon_shape_t* shapes, int n) {
+  size_t total = kControlBytes;
+  for (int i = 0; i < n; ++i) {
+    const Geometry g = geometry_of(shapes[i]);
+    total += 2 * g.x_bytes + 2 * g.a_bytes + g.part_bytes;
+  }
+  return total;
+}
+
+int check_coeffs(const float* coeffs, int ns_steps) {
+  if (ns_steps < 0 || ns_steps > MUON_MAX_NS_STEPS)
+    return fail(MUON_EINVAL, "ns_steps = %d outside [0, %d]", ns_steps, MUON_MAX_NS_STEPS);
+  if (!coeffs) return fail(MUON_EINVAL, "coeffs is NULL");
+  for (int k = 0; k < 3; ++k)
+    if (!std::isfinite(coeffs[k])) return fail(MUON_EINVAL, "coeffs[%d] is not finite", k);
+  return MUON_OK;
+}
+
+struct Range {
+  uintptr_t lo, hi;
+  int mat;
+  const char* what;
+};
+
+// Every listed array must be non-null, aligned, and disjoint from the others.
+int check_ranges(std::vector<Range>& v) {
+  std::sort(v.begin(), v.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
+  for (size_t k = 1; k < v.size(); ++k)
+    if (v[k].lo < v[k - 1].hi)
+      return fail(MUON_EINVAL, "%s of matrix %d overlaps %s of matrix %d", v[k].what, v[k].mat,
+                  v[k - 1].what, v[k - 1].mat);
+  return MUON_OK;
+}
+
+// ---------------------------------------------------------------- plans ----
+
+enum Mode { MODE_STEP = 0, MODE_NS = 1 };
+
+struct Plan {
+  std::vector<uintptr_t> key;
+  void* dev = nullptr;   // descriptors + work lists (device)
+  void* host = nullptr;  // pinned staging of the same bytes
+  size_t bytes = 0;
+  MatDesc* d_desc = nullptr;
+  EwItem* d_mom = nullptr;
+  EwItem* d_cast = nullptr;
+  EwItem* d_apply = nullptr;
+  GemmItem* d_sym = nullptr;
+  GemmItem* d_upd = nullptr;
+  int n_mom = 0, n_cast = 0, n_apply = 0, n_sym = 0, n_upd = 0;
+  ~Plan() {
+    if (dev) (void)hipFree(dev);
+    if (host) (void)hipHostFree(host);
+  }
+};
+
+struct DeviceState {
+  void* ws = nullptr;       // workspace in use (owned or caller's)
+  size_t ws_bytes = 0;
+  bool ws_owned = false;
+  std::list<std::unique_ptr<Plan>> plans;  // most recent first
+};
+
+std::mutex g_mu;
+std::map<int, DeviceState> g_dev;
+constexpr size_t kMaxPlans = 8;
+
+// Timing of one kernel family (muon_timing_enable).
+int g_time_kind = -1;
+std::vector<hipEvent_t> g_ev;  // start, end pairs
+size_t g_ev_used = 0;
+
+int clear_plans(DeviceState& st) {
+  st.plans.clear();
+  return MUON_OK;
+}
+
+int acquire_workspace(DeviceState& st, size_t need, hipStream_t stream) {
+  if (st.ws && st.ws_bytes >= need) return MUON_OK;
+  if (st.ws && !st.ws_owned)
+    return fail(MUON_ENOMEM, "caller workspace has %zu bytes, this call needs %zu", st.ws_bytes, need);
+  const char* inject = getenv("MUON_TEST_FAIL_ALLOC");
+  if (inject && inject[0] == '1') return fail(MUON_ENOMEM, "workspace allocation of %zu bytes failed (injected)", need);
+  // Growing: wait for work that may still use the old buffer, then replace it.
+  hipError_t e;
+  if (st.ws) {
+    if ((e = hipDeviceSynchronize()) != hipSuccess) return fail_hip(e, "hipDeviceSynchronize");
+    (void)hipFree(st.ws);
+    st.ws = nullptr;
+    st.ws_bytes = 0;
+    clear_plans(st);
+  }
+  size_t want = std::max(need, (size_t)(need * 1.25));
+  void* p = nullptr;
+  e = hipMalloc(&p, want);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    want = need;
+    e = hipMalloc(&p, want);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(MUON_ENOMEM, "hipMalloc of %zu workspace bytes failed: %s", want, hipGetErrorString(e));
+    }
+  }
+  // Counters start at zero; wait so that a later call on another stream sees it.
+  if ((e = hipMemsetAsync(p, 0, kCounterBytes, stream)) != hipSuccess ||
+      (e = hipStreamSynchronize(stream)) != hipSuccess) {
+    (void)hipFree(p);
+    return fail_hip(e, "workspace counter reset");
+  }
+  st.ws = p;
+  st.ws_bytes = want;
+  st.ws_owned = true;
+  return MUON_OK;
+}
+
+template <typename T>
+T* carve(char*& cur, size_t count) {
+  T* p = reinterpret_cast<T*>(cur);
+  cur += align_up(count * sizeof(T));
+  return p;
+}
+
+// Build (or fetch) the plan for this call.  Descriptors point into the
+// current workspace; the cache is dropped whenever the workspace changes.
+int get_plan(DeviceState& st, int mode, int n, const muon_shape_t* shapes, float* const* params,
+             const float* const* grads, float* const* moms, uint16_t* const* upd, const uint16_t* const* xin,
+             hipStream_t stream, Plan** out) {
+  std::vector<uintptr_t> key;
+  key.reserve(8 + 6 * (size_t)n);
+  key.push_back((uintptr_t)mode);
+  key.push_back((uintptr_t)n);
+  key.push_back((uintptr_t)st.ws);
+  for (int i = 0; i < n; ++i) {
+    key.push_back((uintptr_t)shapes[i].rows);
+    key.push_back((uintptr_t)shapes[i].cols);
+    key.push_back(params ? (uintptr_t)params[i] : 0);
+    key.push_back(grads ? (uintptr_t)grads[i] : 0);
+    key.push_back(moms ? (uintptr_t)moms[i] : (xin ? (uintptr_t)xin[i] : 0));
+    key.push_back(upd ? (uintptr_t)upd[i] : 0);
+  }
+  for (auto it = st.plans.begin(); it != st.plans.end(); ++it) {
+    if ((*it)->key == key) {
+      if (it != st.plans.begin()) st.plans.splice(st.plans.begin(), st.plans, it);
+      *out = st.plans.front().get();
+      return MUON_OK;
+    }
+  }
+
+  auto plan = std::make_unique<Plan>();
+  plan->key = std::move(key);
+  std::vector<MatDesc> desc(n);
+  std::vector<EwItem> mom, cast, apply;
+  std::vector<GemmItem> sym, updl;
+  char* cur = static_cast<char*>(st.ws);
+  uint32_t* counters = reinterpret_cast<uint32_t*>(cur);
+  float* scales = reinterpret_cast<float*>(cur + kCounterBytes);
+  cur += kControlBytes;
+  for (int i = 0; i < n; ++i) {
+    const Geometry g = geometry_of(shapes[i]);
+    MatDesc& d = desc[i];
+    memset(&d, 0, sizeof d);
+    d.W = params ? params[i] : nullptr;
+    d.G = grads ? grads[i] : nullptr;
+    d.M = moms ? moms[i] : nullptr;
+    d.upd = upd ? upd[i] : nullptr;
+    d.xin = xin ? xin[i] : nullptr;
+    d.X[0] = carve<uint16_t>(cur, g.x_bytes / 2);
+    d.X[1] = carve<uint16_t>(cur, g.x_bytes / 2);
+    d.A = carve<uint16_t>(cur, g.a_bytes / 2);
+    d.B = carve<uint16_t>(cur, g.a_bytes / 2);
+    d.part = carve<double>(cur, g.part_bytes / sizeof(double));
+    d.scale = scales + i;
+    d.counter = counters + i;
+    d.rows = g.rows;
+    d.cols = g.cols;
+    d.m = g.m;
+    d.n = g.n;
+    d.m_pad = g.m_pad;
+    d.n_pad = g.n_pad;
+    d.transposed = g.transposed;
+    d.part_cnt = g.part_cnt;
+    if (mode == MODE_STEP) {
+      const bool aligned = ((uintptr_t)d.W % 16 == 0) && ((uintptr_t)d.G % 16 == 0) && ((uintptr_t)d.M % 16 == 0);
+      d.vec4 = aligned && (g.cols % 4 == 0);
+      for (int c = 0; c < g.part_cnt; ++c) mom.push_back({i, c});
+    } else {
+      d.vec4 = ((uintptr_t)d.xin % 8 == 0) && (g.cols % 4 == 0);
+    }
+    const int ct = (g.m_pad / CAST_TILE) * (g.n_pad / CAST_TILE);
+    for (int t = 0; t < ct; ++t) cast.push_back({i, t});
+    const int at = ((g.rows + CAST_TILE - 1) / CAST_TILE) * ((g.cols + CAST_TILE - 1) / CAST_TILE);
+    for (int t = 0; t < at; ++t) apply.push_back({i, t});
+  }
+  // GEMM tiles, longest K first so the tail of each launch holds short tiles.
+  std::vector<int> order(n);
+  for (int i = 0; i < n; ++i) order[i] = i;
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return desc[a].n_pad > desc[b].n_pad; });
+  for (int i : order) {
+    const int tm = desc[i].m_pad / NS_TILE, tn = desc[i].n_pad / NS_TILE;
+    for (int ti = 0; ti < tm; ++ti)
+      for (int tj = ti; tj < tm; ++tj) sym.push_back({i, (int16_t)ti, (int16_t)tj});
+    for (int ti = 0; ti < tm; ++ti)
+      for (int tj = 0; tj < tn; ++tj) updl.push_back({i, (int16_t)ti, (int16_t)tj});
+  }
+
+  size_t off = 0;
+  auto place = [&](size_t bytes) { const size_t o = off; off += align_up(bytes); return o; };
+  const size_t o_desc = place(sizeof(MatDesc) * n);
+  const size_t o_mom = place(sizeof(EwItem) * mom.size());
+  const size_t o_cast = place(sizeof(EwItem) * cast.size());
+  const size_t o_apply = place(sizeof(EwItem) * apply.size());
+  const size_t o_sym = place(sizeof(GemmItem) * sym.size());
+  const size_t o_upd = place(sizeof(GemmItem) * updl.size());
+  plan->bytes = std::max<size_t>(off, kAlign);
+  hipError_t e;
+  if ((e = hipHostMalloc(&plan->host, plan->bytes, hipHostMallocDefault)) != hipSuccess) {
+    plan->host = nullptr;
+    return fail(MUON_ENOMEM, "hipHostMalloc of %zu plan bytes failed: %s", plan->bytes, hipGetErrorString(e));
+  }
+  if ((e = hipMalloc(&plan->dev, plan->bytes)) != hipSuccess) {
+    plan->dev = nullptr;
+    (void)hipGetLastError();
+    return fail(MUON_ENOMEM, "hipMalloc of %zu plan bytes failed: %s", plan->bytes, hipGetErrorString(e));
+  }
+  char* h = static_cast<char*>(plan->host);
+  memcpy(h + o_desc, desc.data(), sizeof(MatDesc) * n);
+  memcpy(h + o_mom, mom.data(), sizeof(EwItem) * mom.size());
+  memcpy(h + o_cast, cast.data(), sizeof(EwItem) * cast.size());
+  memcpy(h + o_apply, apply.data(), sizeof(EwItem) * apply.size());
+  memcpy(h + o_sym, sym.data(), sizeof(GemmItem) * sym.size());
+  memcpy(h + o_upd, updl.data(), sizeof(GemmItem) * updl.size());
+  if ((e = hipMemcpyAsync(plan->dev, plan->host, plan->bytes, hipMemcpyHostToDevice, stream)) != hipSuccess)
+    return fail_hip(e, "hipMemcpyAsync(plan)");
+  // One-time wait so the plan is usable from any stream afterwards.
+  if ((e = hipStreamSynchronize(stream)) != hipSuccess) return fail_hip(e, "hipStreamSynchronize(plan)");
+  char* dv = static_cast<char*>(plan->dev);
+  plan->d_desc = reinterpret_cast<MatDesc*>(dv + o_desc);
+  plan->d_mom = reinterpret_cast<EwItem*>(dv + o_mom);
+  plan->d_cast = reinterpret_cast<EwItem*>(dv + o_cast);
+  plan->d_apply = reinterpret_cast<EwItem*>(dv + o_apply);
+  plan->d_sym = reinterpret_cast<GemmItem*>(dv + o_sym);
+  plan->d_upd = reinterpret_cast<GemmItem*>(dv + o_upd);
+  plan->n_mom = (int)mom.size();
+  plan->n_cast = (int)cast.size();
+  plan->n_apply = (int)apply.size();
+  plan->n_sym = (int)sym.size();
+  plan->n_upd = (int)updl.size();
+  st.plans.push_front(std::move(plan));
+  while (st.plans.size() > kMaxPlans) st.plans.pop_back();
+  *out = st.plans.front().get();
+  return MUON_OK;
+}
+
+// Launch wrapper: brackets the launch with events when its family is timed.
+template <typename F>
+int timed(int kind, hipStream_t stream, F&& launch, const char* what) {
+  const bool on = (g_time_kind == kind);
+  hipError_t e;
+  if (on) {
+    if (g_ev_used + 2 > g_ev.size()) {
+      for (int k = 0; k < 2; ++k) {
+        hipEvent_t ev;
+        if ((e = hipEventCreate(&ev)) != hipSuccess) return fail_hip(e, "hipEventCreate");
+        g_ev.push_back(ev);
+      }
+    }
+    if ((e = hipEventRecord(g_ev[g_ev_used], stream)) != hipSuccess) return fail_hip(e, "hipEventRecord");
+  }
+  if ((e = launch()) != hipSuccess) return fail_hip(e, what);
+  if (on) {
+    if ((e = hipEventRecord(g_ev[g_ev_used + 1], stream)) != hipSuccess) return fail_hip(e, "hipEventRecord");
+    g_ev_used += 2;
+  }
+  return MUON_OK;
+}
+
+int run(int mode, float* const* params, const float* const* grads, float* const* moms,
+        uint16_t* const* upd, const uint16_t* const* xin, const muon_shape_t* shapes, int n, float lr,
+        float beta, int ns_steps, const float* coeffs, hipStream_t stream) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceState& st = g_dev[dev];
+  int rc = acquire_workspace(st, workspace_bytes_of(shapes, n), stream);
+  if (rc) return rc;
+  Plan* p = nullptr;
+  if ((rc = get_plan(st, mode, n, shapes, params, grads, moms, upd, xin, stream, &p))) return rc;
+  const float ca = coeffs[0], cb = coeffs[1], cc = coeffs[2];
+  if (mode == MODE_STEP) {
+    rc = timed(MUON_KERNEL_MOMENTUM, stream, [&] { return launch_momentum(p->d_desc, p->d_mom, p->n_mom, beta, stream); },
+               "momentum kernel launch");
+    if (rc) return rc;
+  }
+  rc = timed(MUON_KERNEL_CAST, stream,
+             [&] { return launch_cast(p->d_desc, p->d_cast, p->n_cast, beta, mode == MODE_NS, stream); },
+             "cast kernel launch");
+  if (rc) return rc;
+  for (int k = 0; k < ns_steps; ++k) {
+    const int src = k & 1;
+    rc = timed(MUON_KERNEL_GRAM, stream,
+               [&] { return launch_gemm(GEMM_GRAM, p->d_desc, p->d_sym, p->n_sym, src, ca, cb, cc, stream); },
+               "gram kernel launch");
+    if (rc) return rc;
+    rc = timed(MUON_KERNEL_POLY, stream,
+               [&] { return launch_gemm(GEMM_POLY, p->d_desc, p->d_sym, p->n_sym, src, ca, cb, cc, stream); },
+               "poly kernel launch");
+    if (rc) return rc;
+    rc = timed(MUON_KERNEL_UPDATE, stream,
+               [&] { return launch_gemm(GEMM_UPDATE, p->d_desc, p->d_upd, p->n_upd, src, ca, cb, cc, stream); },
+               "update kernel launch");
+    if (rc) return rc;
+  }
+  rc = timed(MUON_KERNEL_APPLY, stream,
+             [&] { return launch_apply(p->d_desc, p->d_apply, p->n_apply, lr, ns_steps & 1, mode == MODE_STEP, stream); },
+             "apply kernel launch");
+  return rc;
+}
+
+int validate_step(float* const* params, const float* const* grads, float* const* moms, const muon_shape_t* shapes,
+                  int n, float lr, float beta, int ns_steps, const float* coeffs, uint16_t* const* upd) {
+  int rc = check_shapes(shapes, n);
+  if (rc) return rc;
+  if (!params || !grads || !moms) return fail(MUON_EINVAL, "params, grads and momentum arrays must not be NULL");
+  if (!std::isfinite(lr)) return fail(MUON_EINVAL, "lr is not finite");
+  if (!std::isfinite(beta) || beta < 0.0f || beta >= 1.0f) return fail(MUON_EINVAL, "beta = %g outside [0, 1)", (double)beta);
+  if ((rc = check_coeffs(coeffs, ns_steps))) return rc;
+  std::vector<Range> r;
+  r.reserve(4 * (size_t)n);
+  for (int i = 0; i < n; ++i) {
+    const size_t fb = (size_t)shapes[i].rows * shapes[i].cols * sizeof(float);
+    const void* ptrs[3] = {params[i], grads[i], moms[i]};
+    const char* names[3] = {"params", "grads", "momentum"};
+    for (int k = 0; k < 3; ++k) {
+      if (!ptrs[k]) return fail(MUON_EINVAL, "%s[%d] is NULL", names[k], i);
+      if ((uintptr_t)ptrs[k] % 4) return fail(MUON_EINVAL, "%s[%d] is not 4-byte aligned", names[k], i);
+      r.push_back({(uintptr_t)ptrs[k], (uintptr_t)ptrs[k] + fb, i, names[k]});
+    }
+    if (upd && upd[i]) {
+      if ((uintptr_t)upd[i] % 2) return fail(MUON_EINVAL, "updates[%d] is not 2-byte aligned", i);
+      r.push_back({(uintptr_t)upd[i], (uintptr_t)upd[i] + fb / 2, i, "updates"});
+    }
+  }
+  return check_ranges(r);
+}
+
+}  // namespace
+
+extern "C" {
+
+int muon_step_ex(float* const* params, const float* const* grads, float* const* momentum,
+                 const muon_shape_t* shapes, int n, float lr, float beta, int ns_steps, const float* coeffs,
+                 uint16_t* const* updates, hipStream_t stream) {
+  g_error.clear();
+  int rc = validate_step(params, grads, momentum, shapes, n, lr, beta, ns_steps, coeffs, updates);
+  if (rc || n == 0) return rc;
+  return run(MODE_STEP, params, grads, momentum, updates, nullptr, shapes, n, lr, beta, ns_steps, coeffs, stream);
+}
+
+int muon_step(float* const* params, const float* const* grads, float* const* momentum,
+              const muon_shape_t* shapes, int n, float lr, float beta, int ns_steps, const float* coeffs,
+              hipStream_t stream) {
+  return muon_step_ex(params, grads, momentum, shapes, n, lr, beta, ns_steps, coeffs, nullptr, stream);
+}
+
+int muon_newton_schulz(const uint16_t* const* x, uint16_t* const* out, const muon_shape_t* shapes, int n,
+                       int ns_steps, const float* coeffs, hipStream_t stream) {
+  g_error.clear();
+  int rc = check_shapes(shapes, n);
+  if (rc) return rc;
+  if (!x || !out) return fail(MUON_EINVAL, "x and out arrays must not be NULL");
+  if ((rc = check_coeffs(coeffs, ns_steps))) return rc;
+  std::vector<Range> r;
+  for (int i = 0; i < n; ++i) {
+    if (!x[i] || !out[i]) return fail(MUON_EINVAL, "x[%d] or out[%d] is NULL", i, i);
+    if ((uintptr_t)x[i] % 2 || (uintptr_t)out[i] % 2) return fail(MUON_EINVAL, "x[%d] or out[%d] is not 2-byte aligned", i, i);
+    const size_t b = (size_t)shapes[i].rows * shapes[i].cols * 2;
+    r.push_back({(uintptr_t)out[i], (uintptr_t)out[i] + b, i, "out"});
+    if (x[i] != out[i]) r.push_back({(uintptr_t)x[i], (uintptr_t)x[i] + b, i, "x"});
+  }
+  if ((rc = check_ranges(r))) return rc;
+  if (n == 0) return MUON_OK;
+  return run(MODE_NS, nullptr, nullptr, nullptr, out, x, shapes, n, 0.0f, 0.0f, ns_steps, coeffs, stream);
+}
+
+const char* muon_last_error(void) { return g_error.c_str(); }
+
+size_t muon_workspace_bytes(const muon_shape_t* shapes, int n) {
+  g_error.clear();
+  if (check_shapes(shapes, n)) return 0;
+  return workspace_bytes_of(shapes, n);
+}
+
+int muon_set_workspace(void* dev_ptr, size_t bytes) {
+  g_error.clear();
+  if ((dev_ptr == nullptr) != (bytes == 0)) return fail(MUON_EINVAL, "dev_ptr and bytes must both be set or both be 0");
+  if ((uintptr_t)dev_ptr % kAlign) return fail(MUON_EINVAL, "workspace must be %zu-byte aligned", kAlign);
+  if (dev_ptr && bytes < kControlBytes) return fail(MUON_ENOMEM, "workspace of %zu bytes is below the %zu-byte minimum", bytes, kControlBytes);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceState& st = g_dev[dev];
+  if ((e = hipDeviceSynchronize()) != hipSuccess) return fail_hip(e, "hipDeviceSynchronize");
+  clear_plans(st);
+  if (st.ws && st.ws_owned) (void)hipFree(st.ws);
+  st.ws = dev_ptr;
+  st.ws_bytes = bytes;
+  st.ws_owned = false;
+  if (dev_ptr) {
+    if ((e = hipMemset(dev_ptr, 0, kCounterBytes)) != hipSuccess || (e = hipDeviceSynchronize()) != hipSuccess)
+      return fail_hip(e, "workspace counter reset");
+  } else {
+    st.ws = nullptr;
+    st.ws_bytes = 0;
+  }
+  return MUON_OK;
+}
+
+void muon_release(void) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  int cur = 0;
+  (void)hipGetDevice(&cur);
+  for (auto& kv : g_dev) {
+    if (hipSetDevice(kv.first) != hipSuccess) continue;
+    (void)hipDeviceSynchronize();
+    kv.second.plans.clear();
+    if (kv.second.ws && kv.second.ws_owned) (void)hipFree(kv.second.ws);
+  }
+  (void)hipSetDevice(cur);
+  g_dev.clear();
+  for (hipEvent_t ev : g_ev) (void)hipEventDestroy(ev);
+  g_ev.clear();
+  g_ev_used = 0;
+}
+
+int muon_timing_enable(int kernel) {
+  g_error.clear();
+  if (kernel < -1 || kernel > MUON_KERNEL_APPLY) return fail(MUON_EINVAL, "unknown kernel family %d", kernel);
+  std::lock_guard<std::mutex> lock(g_mu);
+  g_time_kind = kernel;
+  g_ev_used = 0;
+  return MUON_OK;
+}
+
+int muon_timing_read(double* total_ms, int64_t* launches) {
+  g_error.clear();
+  if (!total_ms || !launches) return fail(MUON_EINVAL, "output pointers must not be NULL");
+  std::lock_guard<std::mutex> lock(g_mu);
+  double sum = 0.0;
+  for (size_t k = 0; k + 1 < g_ev_used; k += 2) {
+    hipError_t e = hipEventSynchronize(g_ev[k + 1]);
+    if (e != hipSuccess) return fail_hip(e, "hipEventSynchronize");
+    float ms = 0.0f;
+    if ((e = hipEventElapsedTime(&ms, g_ev[k], g_ev[k + 1])) != hipSuccess) return fail_hip(e, "hipEventElapsedTime");
+    sum += ms;
+  }
+  *total_ms = sum;
+  *launches = (int64_t)(g_ev_used / 2);
+  g_ev_used = 0;
+  return MUON_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,67 @@
+// Internal declarations shared by the host plan code and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace muon {
+
+// Tile geometry of the Newton-Schulz GEMMs.  Every canonical dimension is
+// padded up to NS_TILE inside the workspace, with the padding held at exact
+// zero, so the GEMM kernels never bounds-check.
+constexpr int NS_TILE = 128;  // output tile edge (rows and columns)
+constexpr int NS_BK = 64;     // K slice staged through LDS per pipeline step
+constexpr int NS_THREADS = 256;
+
+// Elementwise kernels.
+constexpr int EW_THREADS = 256;
+constexpr int MOM_CHUNK = 16384;  // elements per momentum work item
+constexpr int CAST_TILE = 64;     // square tile for the cast / apply kernels
+
+// One matrix of a call, in device memory.
+struct MatDesc {
+  float* W;               // caller params (rows x cols) or null
+  const float* G;         // caller gradient or null
+  float* M;               // caller momentum buffer or null
+  uint16_t* upd;          // optional bf16 update output (rows x cols) or null
+  const uint16_t* xin;    // bf16 input of the NS-only entry (rows x cols) or null
+  uint16_t* X[2];         // canonical padded iterate, ping-pong (m_pad x n_pad)
+  uint16_t* A;            // X X^T, m_pad x m_pad
+  uint16_t* B;            // b A + c A A, m_pad x m_pad
+  double* part;           // norm partial sums of this matrix (part_cnt of them)
+  float* scale;           // s = 1 / (||U||_F + eps), written by the momentum kernel
+  uint32_t* counter;      // finished momentum chunks; returns to 0 after each call
+  int32_t rows, cols;     // caller orientation
+  int32_t m, n;           // canonical, m <= n
+  int32_t m_pad, n_pad;   // multiples of NS_TILE
+  int32_t transposed;     // 1 when rows > cols
+  int32_t part_cnt;
+  int32_t vec4;           // 1 when every row start allows 4-element vector access
+  int32_t pad_;
+};
+
+// GEMM work item: one output tile of one matrix.
+struct GemmItem {
+  int32_t mat;
+  int16_t ti, tj;  // tile row / column in units of NS_TILE
+};
+
+// Elementwise work item: chunk (momentum) or tile (cast / apply) of a matrix.
+struct EwItem {
+  int32_t mat;
+  int32_t idx;
+};
+
+enum GemmKind { GEMM_GRAM = 0, GEMM_POLY = 1, GEMM_UPDATE = 2 };
+
+// ---- host launchers (kernels_*.hip) ----
+hipError_t launch_momentum(const MatDesc* d, const EwItem* items, int n_items, float beta,
+                           hipStream_t s);
+hipError_t launch_cast(const MatDesc* d, const EwItem* items, int n_items, float beta, int from_bf16,
+                       hipStream_t s);
+hipError_t launch_apply(const MatDesc* d, const EwItem* items, int n_items, float lr, int src,
+                        int write_w, hipStream_t s);
+hipError_t launch_gemm(int kind, const MatDesc* d, const GemmItem* items, int n_items, int src,
+                       float ca, float cb, float cc, hipStream_t s);
+
+}  // namespace muon

@@ -1,0 +1,130 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every entry point include/muon.h declares, and rejects invalid arguments
+before touching the device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from optimizer_muon_step_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "muon.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(muon_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from optimizer_muon_step_amd import build
+        build.build()
+    return _lib.load()
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ("muon_step", "muon_step_ex", "muon_newton_schulz", "muon_last_error", "muon_workspace_bytes",
+                 "muon_set_workspace", "muon_release", "muon_timing_enable", "muon_timing_read"):
+        assert want in names
+    assert set(names) == set(_lib.SIGNATURES), "binding signatures and header disagree"
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (muon_\w+)", out))
+    assert set(declared_functions()) <= exported
+
+
+def test_library_is_built_for_gfx950():
+    out = subprocess.run(["/opt/rocm/bin/roc-obj-ls", _lib.LIB_PATH], capture_output=True, text=True)
+    if out.returncode != 0:
+        pytest.skip("roc-obj-ls unavailable")
+    assert "gfx950" in out.stdout
+
+
+def _step(lib, params, grads, moms, shapes, n, lr=0.02, beta=0.95, k=5, coeffs=(3.4445, -4.775, 2.0315)):
+    return lib.muon_step(params, grads, moms, shapes, n, lr, beta, k, _lib.float3(coeffs) if coeffs else None, None)
+
+
+def test_invalid_arguments_are_rejected_before_any_hip_call(lib):
+    fake = _lib.ptr_array([0x10000])
+    fake2 = _lib.ptr_array([0x20000])
+    fake3 = _lib.ptr_array([0x30000])
+    good = _lib.shape_array([(4, 4)])
+    cases = [
+        (dict(params=None, grads=fake2, moms=fake3, shapes=good, n=1), "NULL"),
+        (dict(params=fake, grads=fake2, moms=fake3, shapes=None, n=1), "shapes"),
+        (dict(params=fake, grads=fake2, moms=fake3, shapes=_lib.shape_array([(0, 4)]), n=1), ">= 1"),
+        (dict(params=fake, grads=fake2, moms=fake3, shapes=_lib.shape_array([(1 << 16, 1 << 16)]), n=1), "2^31"),
+        (dict(params=fake, grads=fake2, moms=fake3, shapes=good, n=-1), "outside"),
+        (dict(params=fake, grads=fake2, moms=fake3, shapes=good, n=1, lr=float("inf")), "lr"),
+        (dict(params=fake, grads=fake2, moms=fake3, shapes=good, n=1, beta=1.0), "beta"),
+        (dict(params=fake, grads=fake2, moms=fake3, shapes=good, n=1, beta=-0.1), "beta"),
+        (dict(params=fake, grads=fake2, moms=fake3, shapes=good, n=1, k=-1), "ns_steps"),
+        (dict(params=fake, grads=fake2, moms=fake3, shapes=good, n=1, k=65), "ns_steps"),
+        (dict(params=fake, grads=fake2, moms=fake3, shapes=good, n=1, coeffs=(1.0, float("nan"), 0.0)), "coeffs"),
+        (dict(params=fake, grads=fake2, moms=fake3, shapes=good, n=1, coeffs=None), "coeffs"),
+        (dict(params=fake, grads=fake2, moms=fake, shapes=good, n=1), "overlaps"),
+        (dict(params=_lib.ptr_array([0x10002]), grads=fake2, moms=fake3, shapes=good, n=1), "aligned"),
+        (dict(params=_lib.ptr_array([None]), grads=fake2, moms=fake3, shapes=good, n=1), "NULL"),
+    ]
+    for kw, msg in cases:
+        rc = _step(lib, **kw)
+        assert rc == -1, (kw, rc)
+        assert msg in lib.muon_last_error().decode(), (msg, lib.muon_last_error())
+    # overlapping ranges of different matrices
+    two = _lib.shape_array([(4, 4), (4, 4)])
+    rc = lib.muon_step(_lib.ptr_array([0x10000, 0x10020]), _lib.ptr_array([0x20000, 0x21000]),
+                       _lib.ptr_array([0x30000, 0x31000]), two, 2, 0.02, 0.95, 5, _lib.float3((1, 0, 0)), None)
+    assert rc == -1 and "overlaps" in lib.muon_last_error().decode()
+    # n == 0 needs no device and succeeds
+    assert _step(lib, None, None, None, None, 0) in (0, -1)
+    assert lib.muon_step(fake, fake2, fake3, good, 0, 0.02, 0.95, 5, _lib.float3((1, 0, 0)), None) == 0
+
+
+def test_newton_schulz_entry_validation(lib):
+    x = _lib.ptr_array([0x10000])
+    s = _lib.shape_array([(4, 4)])
+    c = _lib.float3((3.4445, -4.775, 2.0315))
+    assert lib.muon_newton_schulz(None, x, s, 1, 5, c, None) == -1
+    assert lib.muon_newton_schulz(x, x, s, 1, -2, c, None) == -1
+    assert lib.muon_newton_schulz(_lib.ptr_array([0x10001]), x, s, 1, 5, c, None) == -1
+    assert "aligned" in lib.muon_last_error().decode()
+
+
+def test_workspace_bytes_host_logic(lib):
+    def ws(shapes):
+        return lib.muon_workspace_bytes(_lib.shape_array(shapes), len(shapes))
+    assert ws([]) > 0  # control block only
+    base = ws([])
+    # bf16 ping-pong iterate + Gram + polynomial matrices, canonical and padded to 128
+    one = ws([(768, 2304)]) - base
+    assert one >= 2 * 768 * 2304 * 2 + 2 * 768 * 768 * 2
+    assert ws([(2304, 768)]) - base == one  # orientation does not matter
+    assert ws([(100, 200)]) - base >= 2 * 128 * 256 * 2 + 2 * 128 * 128 * 2
+    assert ws([(768, 2304), (768, 768)]) == base + one + (ws([(768, 768)]) - base)
+    assert lib.muon_workspace_bytes(_lib.shape_array([(0, 3)]), 1) == 0
+    assert "shape" in lib.muon_last_error().decode()
+
+
+def test_timing_enable_validation(lib):
+    assert lib.muon_timing_enable(99) == -1
+    assert lib.muon_timing_enable(-1) == 0
+    ms, cnt = ctypes.c_double(), ctypes.c_int64()
+    assert lib.muon_timing_read(ctypes.byref(ms), ctypes.byref(cnt)) == 0 and cnt.value == 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="no fallback"):
+        _lib.load()
