@@ -1,0 +1,228 @@
+#!/usr/bin/env python3
+"""Benchmark: Muon optimizer steps/s on the GPT-2-124M hidden matrices, on one MI355X.
+
+One step = one call of the library's muon_step over all 48 hidden matrices of
+GPT-2-124M (12 layers x 768x2304, 768x768, 768x3072, 3072x768; 84.9 M fp32
+parameters): Nesterov momentum, Frobenius normalisation, 5 bf16 quintic
+Newton-Schulz iterations and the parameter update.  Inputs are seeded
+synthetic gradients of that shape, resident in HBM before timing starts.
+
+Prints one JSON line.  `roofline` is for the dominant kernel (the Newton-Schulz
+update GEMM X <- aX + BX): algorithmic flops per launch / its mean launch time,
+timed with HIP events on the launch stream inside the timed region.
+`cpu_baseline` is the CPU oracle timed on a bounded sample of the same
+workload (some layers), scaled to steps/s.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+LR, BETA, NS_STEPS = 0.02, 0.95, 5
+COEFFS = (3.4445, -4.7750, 2.0315)
+WORKLOAD = "c3"
+
+
+def ns_flops(shapes):
+    """Algorithmic flops per launch of each Newton-Schulz GEMM, counting the
+    symmetry of X X^T and of A A."""
+    gram = poly = upd = 0
+    for r, c in shapes:
+        m, n = min(r, c), max(r, c)
+        gram += m * (m + 1) * n
+        poly += m * m * (m + 1)
+        upd += 2 * m * m * n
+    return gram, poly, upd
+
+
+def traffic_from_profiles(kernel_file):
+    """HBM bytes per launch of the update GEMM, from committed rocprofv3 counter
+    runs, if they were taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "ns_update_c3_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    sha = hashlib.sha256(open(kernel_file, "rb").read()).hexdigest()
+    if rec.get("kernel_source_sha256") != sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(budget_s):
+    """Time the oracle on whole layers of the workload until the budget is used."""
+    import numpy as np
+    from oracle import muon_oracle as om
+    from optimizer_muon_step_amd import workloads as wl
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max(int(i.get("num_threads", 1)) for i in threadpool_info()) if threadpool_info() else 1
+    except Exception:
+        cores = os.cpu_count() or 1
+    specs = wl.config_specs(WORKLOAD)
+    layers = sorted({s.layer for s in specs})
+    elapsed, done = 0.0, 0
+    for layer in layers:
+        idx = [i for i, s in enumerate(specs) if s.layer == layer]
+        mats = [wl.make_matrix(WORKLOAD, i, 1) for i in idx]
+        t0 = time.perf_counter()
+        for m in mats:
+            om.muon_step_matrix(m["W"], m["grads"][0], m["buf"], LR, BETA, NS_STEPS, COEFFS)
+        elapsed += time.perf_counter() - t0
+        done += 1
+        if elapsed >= budget_s:
+            break
+    sec_per_step = elapsed / done * len(layers)
+    return {"value": 1.0 / sec_per_step, "unit": "steps/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} of {len(layers)} layers ({4 * done} of {len(specs)} matrices), one step each, "
+                      f"{elapsed:.1f} s, scaled to the full 48-matrix step"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-breakdown", action="store_true", help="also time every kernel family")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the step shards by whole matrices across ranks, which is not built here)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    import optimizer_muon_step_amd as mu
+    from optimizer_muon_step_amd import workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    mu._lib.load()
+    torch.cuda.set_device(0)
+    specs = wl.config_specs(WORKLOAD)
+    shapes = [(s.rows, s.cols) for s in specs]
+    n_params = sum(r * c for r, c in shapes)
+    W, G, M = [], [], []
+    for i, s in enumerate(specs):
+        W.append(torch.from_numpy(wl.make_params(WORKLOAD, i, s)).cuda())
+        G.append(torch.from_numpy(wl.make_grad(WORKLOAD, i, s, 1)).cuda())
+        M.append(torch.zeros((s.rows, s.cols), dtype=torch.float32, device="cuda"))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def step():
+        mu.muon_step(W, G, M, LR, BETA, NS_STEPS, COEFFS, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region: K steps; the update GEMM's launches are bracketed by HIP
+    # events on this stream.
+    mu.muon_timing_enable(mu.KERNEL_UPDATE)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    upd_ms_total, upd_launches = mu.muon_timing_read()
+    mu.muon_timing_enable(-1)
+    wall_s = t1 - t0
+    ms_per_step = wall_s * 1e3 / args.steps
+    ev_ms_per_step = ev0.elapsed_time(ev1) / args.steps
+
+    gram_f, poly_f, upd_f = ns_flops(shapes)
+    ns_flops_step = NS_STEPS * (gram_f + poly_f + upd_f)
+    upd_ms = upd_ms_total / max(1, upd_launches)
+    upd_tflops = upd_f / (upd_ms * 1e-3) / 1e12
+
+    breakdown = None
+    if args.kernel_breakdown:
+        names = ["momentum", "cast", "gram", "poly", "update", "apply"]
+        per_launch_work = [12 * n_params, 10 * n_params, gram_f, poly_f, upd_f, 10 * n_params]
+        breakdown = {}
+        for k, name in enumerate(names):
+            mu.muon_timing_enable(k)
+            for _ in range(20):
+                step()
+            ms, cnt = mu.muon_timing_read()
+            mu.muon_timing_enable(-1)
+            per = ms / max(1, cnt)
+            if k in (2, 3, 4):
+                ach = per_launch_work[k] / (per * 1e-3) / 1e12
+                breakdown[name] = {"ms_per_launch": round(per, 5), "launches_per_step": cnt // 20,
+                                   "TFLOP/s": round(ach, 1), "frac_bf16_peak": round(ach / PEAK_BF16_TFLOPS, 4)}
+            else:
+                ach = per_launch_work[k] / (per * 1e-3) / 1e9
+                breakdown[name] = {"ms_per_launch": round(per, 5), "launches_per_step": cnt // 20,
+                                   "GB/s": round(ach, 1), "frac_hbm_peak": round(ach / PEAK_HBM_GBS, 4)}
+        torch.cuda.synchronize()
+
+    # A plain copy of known size, outside the timed region: it calibrates
+    # rocprofv3's FETCH_SIZE / WRITE_SIZE counters when this script is profiled.
+    calib = torch.empty(64 * 1024 * 1024, dtype=torch.float32, device="cuda")
+    calib2 = torch.empty_like(calib)
+    calib2.copy_(calib)
+    torch.cuda.synchronize()
+    del calib, calib2
+
+    kernel_file = os.path.join(ROOT, "optimizer_muon_step_amd", "csrc", "kernels_ns.hip")
+    out = {
+        "metric": "Muon steps/s on GPT-2-124M hidden matrices; NS TFLOP/s as % bf16 MFMA peak",
+        "value": round(args.steps / wall_s, 3),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step_hip_events": round(ev_ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "GPT-2-124M hidden set: 12 layers x (768x2304, 768x768, 768x3072, 3072x768), "
+                        "48 fp32 matrices, 84.9M params; grads N(0,1e-3^2) x 10^U(-1,1) per layer",
+            "n_matrices": len(shapes), "n_params": n_params, "ns_steps": NS_STEPS, "lr": LR, "beta": BETA,
+            "coeffs": list(COEFFS),
+        },
+        "ns_tflops_per_step": round(ns_flops_step / 1e12, 4),
+        "ns_tflops_per_s_whole_step": round(ns_flops_step / (ms_per_step * 1e-3) / 1e12, 1),
+        "roofline": {
+            "kernel": "ns_update (X <- aX + BX, bf16 MFMA)",
+            "bound": "mfma",
+            "achieved": round(upd_tflops, 1),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(upd_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic_from_profiles(kernel_file),
+            "flops_per_launch": upd_f,
+            "ms_per_launch": round(upd_ms, 5),
+            "launches": upd_launches,
+        },
+    }
+    if breakdown is not None:
+        out["kernels"] = breakdown
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.cpu_budget)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
