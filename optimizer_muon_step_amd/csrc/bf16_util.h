@@ -11,6 +11,21 @@
 
 namespace muon {
 
+// Pointers read out of descriptors are generic (flat) pointers; flat memory
+// instructions also count against the LDS wait counter, so a pending global
+// prefetch would stall every LDS wait.  Casting to the global address space
+// makes the compiler emit global_load / global_store.
+#define MUON_GLOBAL __attribute__((address_space(1)))
+
+template <typename T>
+__device__ __forceinline__ MUON_GLOBAL T* gptr(T* p) {
+  return (MUON_GLOBAL T*)p;
+}
+template <typename T>
+__device__ __forceinline__ const MUON_GLOBAL T* gptr(const T* p) {
+  return (const MUON_GLOBAL T*)p;
+}
+
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;

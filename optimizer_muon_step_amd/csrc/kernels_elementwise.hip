@@ -22,6 +22,11 @@ namespace {
 
 constexpr int kWaves = EW_THREADS / 64;
 
+// Native vector types: HIP's float4/uint2 classes cannot be assigned through
+// global-address-space pointers.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
 // Fixed-order block sum of one double per thread; the total is valid in thread 0.
 __device__ double block_sum(double v, double* red) {
 #pragma unroll
@@ -42,72 +47,81 @@ __device__ __forceinline__ float nesterov(float g, float m_new, float beta) {
 
 }  // namespace
 
-// One work item = MOM_CHUNK consecutive elements of one matrix.  The block
-// that finishes last for a matrix (counted with a device-scope atomic) sums
-// that matrix's partials in index order and stores s, so the result does not
-// depend on scheduling.
+// One work item = MOM_CHUNK consecutive elements of one matrix; it writes one
+// fp64 partial sum of U^2.  norm_finalize_kernel then reduces each matrix's
+// partials in index order, so the result does not depend on scheduling (and no
+// device-scope fence is needed inside the streaming kernel).  All loads of a
+// batch are issued before any store so the whole batch is in flight at once.
 __global__ __launch_bounds__(EW_THREADS) void momentum_kernel(const MatDesc* __restrict__ descs,
                                                               const EwItem* __restrict__ items,
                                                               float beta) {
+  constexpr int V = MOM_CHUNK / (4 * EW_THREADS);  // float4 per thread
   __shared__ double red[kWaves];
-  __shared__ int is_last;
   const EwItem it = items[blockIdx.x];
   const MatDesc& d = descs[it.mat];
   const int64_t total = (int64_t)d.rows * d.cols;
   const int64_t base = (int64_t)it.idx * MOM_CHUNK;
   const int64_t end = min(base + (int64_t)MOM_CHUNK, total);
-  const float* __restrict__ G = d.G;
-  float* __restrict__ M = d.M;
+  const MUON_GLOBAL float* G = gptr(d.G);
+  MUON_GLOBAL float* M = gptr(d.M);
   double ss = 0.0;
-  int64_t scalar_from = base;
-  if (d.vec4) {
-    const int n4 = (int)((end - base) >> 2);
-    const float4* __restrict__ g4 = reinterpret_cast<const float4*>(G + base);
-    float4* __restrict__ m4 = reinterpret_cast<float4*>(M + base);
-#pragma unroll 4
-    for (int k = threadIdx.x; k < n4; k += EW_THREADS) {
-      const float4 g = g4[k];
-      float4 m = m4[k];
-      m.x = beta * m.x + g.x;
-      m.y = beta * m.y + g.y;
-      m.z = beta * m.z + g.z;
-      m.w = beta * m.w + g.w;
-      m4[k] = m;
-      const float ux = nesterov(g.x, m.x, beta), uy = nesterov(g.y, m.y, beta);
-      const float uz = nesterov(g.z, m.z, beta), uw = nesterov(g.w, m.w, beta);
+  if (d.vec4 && end - base == MOM_CHUNK) {
+    const MUON_GLOBAL f32x4* g4 = reinterpret_cast<const MUON_GLOBAL f32x4*>(G + base);
+    MUON_GLOBAL f32x4* m4 = reinterpret_cast<MUON_GLOBAL f32x4*>(M + base);
+    f32x4 g[V], m[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) g[v] = g4[v * EW_THREADS + threadIdx.x];
+#pragma unroll
+    for (int v = 0; v < V; ++v) m[v] = m4[v * EW_THREADS + threadIdx.x];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      m[v].x = beta * m[v].x + g[v].x;
+      m[v].y = beta * m[v].y + g[v].y;
+      m[v].z = beta * m[v].z + g[v].z;
+      m[v].w = beta * m[v].w + g[v].w;
+      m4[v * EW_THREADS + threadIdx.x] = m[v];
+      const float ux = nesterov(g[v].x, m[v].x, beta), uy = nesterov(g[v].y, m[v].y, beta);
+      const float uz = nesterov(g[v].z, m[v].z, beta), uw = nesterov(g[v].w, m[v].w, beta);
       ss += (double)ux * ux;
       ss += (double)uy * uy;
       ss += (double)uz * uz;
       ss += (double)uw * uw;
     }
-    scalar_from = base + ((int64_t)n4 << 2);
-  }
-  for (int64_t e = scalar_from + threadIdx.x; e < end; e += EW_THREADS) {
-    const float g = G[e];
-    const float m = beta * M[e] + g;
-    M[e] = m;
-    const float u = nesterov(g, m, beta);
-    ss += (double)u * u;
-  }
-  ss = block_sum(ss, red);
-  if (threadIdx.x == 0) {
-    d.part[it.idx] = ss;
-    __threadfence();
-    const unsigned prev = atomicAdd(d.counter, 1u);
-    is_last = (prev == (unsigned)(d.part_cnt - 1));
-  }
-  __syncthreads();
-  if (is_last) {
-    __threadfence();
-    double v = 0.0;
-    for (int k = threadIdx.x; k < d.part_cnt; k += EW_THREADS) v += __builtin_nontemporal_load(&d.part[k]);
-    __syncthreads();
-    v = block_sum(v, red);
-    if (threadIdx.x == 0) {
-      *d.scale = (float)(1.0 / (sqrt(v) + 1e-7));
-      *d.counter = 0u;  // leave the counter at rest for the next call
+  } else {
+    // partial or unaligned chunk: scalar elements, batches of 4V per thread
+    for (int64_t b0 = base; b0 < end; b0 += 4 * V * EW_THREADS) {
+      float g[4 * V], m[4 * V];
+#pragma unroll
+      for (int v = 0; v < 4 * V; ++v) {
+        const int64_t e = b0 + v * EW_THREADS + threadIdx.x;
+        g[v] = e < end ? G[e] : 0.0f;
+        m[v] = e < end ? M[e] : 0.0f;
+      }
+#pragma unroll
+      for (int v = 0; v < 4 * V; ++v) {
+        const int64_t e = b0 + v * EW_THREADS + threadIdx.x;
+        if (e < end) {
+          const float mn = beta * m[v] + g[v];
+          M[e] = mn;
+          const float u = nesterov(g[v], mn, beta);
+          ss += (double)u * u;
+        }
+      }
     }
   }
+  ss = block_sum(ss, red);
+  if (threadIdx.x == 0) d.part[it.idx] = ss;
+}
+
+// One block per matrix: s = 1 / (sqrt(sum of partials) + 1e-7), the sum taken
+// in a fixed order.
+__global__ __launch_bounds__(EW_THREADS) void norm_finalize_kernel(const MatDesc* __restrict__ descs) {
+  __shared__ double red[kWaves];
+  const MatDesc& d = descs[blockIdx.x];
+  double v = 0.0;
+  for (int k = threadIdx.x; k < d.part_cnt; k += EW_THREADS) v += d.part[k];
+  v = block_sum(v, red);
+  if (threadIdx.x == 0) *d.scale = (float)(1.0 / (sqrt(v) + 1e-7));
 }
 
 // Value of canonical element (i, j) taken from source element (r, c); zero
@@ -123,29 +137,29 @@ __device__ __forceinline__ void load4_src(const MatDesc& d, int r, int c, float 
   const int64_t off = (int64_t)r * d.cols + c;
   if (FROM_BF16) {
     if (d.vec4 && c + 3 < d.cols) {
-      const uint2 w = *reinterpret_cast<const uint2*>(d.xin + off);
+      const u32x2 w = *reinterpret_cast<const MUON_GLOBAL u32x2*>(gptr(d.xin) + off);
       out[0] = bf16_lo(w.x);
       out[1] = bf16_hi(w.x);
       out[2] = bf16_lo(w.y);
       out[3] = bf16_hi(w.y);
     } else {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) out[k] = (c + k < d.cols) ? bf16_bits_to_f32(d.xin[off + k]) : 0.0f;
+      for (int k = 0; k < 4; ++k) out[k] = (c + k < d.cols) ? bf16_bits_to_f32(gptr(d.xin)[off + k]) : 0.0f;
     }
     return;
   }
   float g[4], m[4];
   if (d.vec4 && c + 3 < d.cols) {
-    const float4 g4 = *reinterpret_cast<const float4*>(d.G + off);
-    const float4 m4 = *reinterpret_cast<const float4*>(d.M + off);
+    const f32x4 g4 = *reinterpret_cast<const MUON_GLOBAL f32x4*>(gptr(d.G) + off);
+    const f32x4 m4 = *reinterpret_cast<const MUON_GLOBAL f32x4*>(gptr(d.M) + off);
     g[0] = g4.x; g[1] = g4.y; g[2] = g4.z; g[3] = g4.w;
     m[0] = m4.x; m[1] = m4.y; m[2] = m4.z; m[3] = m4.w;
   } else {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const bool in = c + k < d.cols;
-      g[k] = in ? d.G[off + k] : 0.0f;
-      m[k] = in ? d.M[off + k] : 0.0f;
+      g[k] = in ? gptr(d.G)[off + k] : 0.0f;
+      m[k] = in ? gptr(d.M)[off + k] : 0.0f;
     }
   }
 #pragma unroll
@@ -164,39 +178,38 @@ __global__ __launch_bounds__(EW_THREADS) void cast_kernel(const MatDesc* __restr
   const int i0 = (it.idx / tiles_j) * CAST_TILE;
   const int j0 = (it.idx % tiles_j) * CAST_TILE;
   const float s = FROM_BF16 ? 1.0f : *d.scale;
-  uint16_t* __restrict__ X = d.X[0];
+  MUON_GLOBAL uint16_t* X = gptr(d.X[0]);
   const int tc = (threadIdx.x & 15) * 4;
   const int tr = threadIdx.x >> 4;
+  float v[4][4];
   if (!d.transposed) {
+    // all loads first, then all stores
+#pragma unroll
+    for (int q = 0; q < 4; ++q) load4_src<FROM_BF16>(d, i0 + tr + 16 * q, j0 + tc, beta, s, v[q]);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int i = i0 + tr + 16 * q;
-      const int j = j0 + tc;
-      float v[4];
-      load4_src<FROM_BF16>(d, i, j, beta, s, v);
-      uint2 w;
-      w.x = pack_bf16x2(v[0], v[1]);
-      w.y = pack_bf16x2(v[2], v[3]);
-      *reinterpret_cast<uint2*>(X + (int64_t)i * d.n_pad + j) = w;
+      u32x2 w;
+      w.x = pack_bf16x2(v[q][0], v[q][1]);
+      w.y = pack_bf16x2(v[q][2], v[q][3]);
+      *reinterpret_cast<MUON_GLOBAL u32x2*>(X + (int64_t)(i0 + tr + 16 * q) * d.n_pad + j0 + tc) = w;
     }
   } else {
     // canonical (i, j) comes from source (j, i): stage a source tile whose
     // rows are canonical columns j0.. and columns are canonical rows i0..
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      float v[4];
-      load4_src<FROM_BF16>(d, j0 + tr + 16 * q, i0 + tc, beta, s, v);
+    for (int q = 0; q < 4; ++q) load4_src<FROM_BF16>(d, j0 + tr + 16 * q, i0 + tc, beta, s, v[q]);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) T[tr + 16 * q][tc + k] = v[k];
-    }
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) T[tr + 16 * q][tc + k] = v[q][k];
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int il = tr + 16 * q;
-      uint2 w;
+      u32x2 w;
       w.x = pack_bf16x2(T[tc + 0][il], T[tc + 1][il]);
       w.y = pack_bf16x2(T[tc + 2][il], T[tc + 3][il]);
-      *reinterpret_cast<uint2*>(X + (int64_t)(i0 + il) * d.n_pad + j0 + tc) = w;
+      *reinterpret_cast<MUON_GLOBAL u32x2*>(X + (int64_t)(i0 + il) * d.n_pad + j0 + tc) = w;
     }
   }
 }
@@ -211,7 +224,7 @@ __global__ __launch_bounds__(EW_THREADS) void apply_kernel(const MatDesc* __rest
   const int tiles_c = (d.cols + CAST_TILE - 1) / CAST_TILE;
   const int r0 = (it.idx / tiles_c) * CAST_TILE;
   const int c0 = (it.idx % tiles_c) * CAST_TILE;
-  const uint16_t* __restrict__ X = d.X[src];
+  const MUON_GLOBAL uint16_t* X = gptr(d.X[src]);
   const int tc = (threadIdx.x & 15) * 4;
   const int tr = threadIdx.x >> 4;
   uint32_t h[4][4];
@@ -219,7 +232,7 @@ __global__ __launch_bounds__(EW_THREADS) void apply_kernel(const MatDesc* __rest
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int r = min(r0 + tr + 16 * q, d.m_pad - 1);
-      const uint2 w = *reinterpret_cast<const uint2*>(X + (int64_t)r * d.n_pad + c0 + tc);
+      const u32x2 w = *reinterpret_cast<const MUON_GLOBAL u32x2*>(X + (int64_t)r * d.n_pad + c0 + tc);
       h[q][0] = w.x & 0xffffu;
       h[q][1] = w.x >> 16;
       h[q][2] = w.y & 0xffffu;
@@ -230,7 +243,7 @@ __global__ __launch_bounds__(EW_THREADS) void apply_kernel(const MatDesc* __rest
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int xr = c0 + tr + 16 * q;
-      const uint2 w = *reinterpret_cast<const uint2*>(X + (int64_t)xr * d.n_pad + r0 + tc);
+      const u32x2 w = *reinterpret_cast<const MUON_GLOBAL u32x2*>(X + (int64_t)xr * d.n_pad + r0 + tc);
       T[tr + 16 * q][tc + 0] = (uint16_t)(w.x & 0xffffu);
       T[tr + 16 * q][tc + 1] = (uint16_t)(w.x >> 16);
       T[tr + 16 * q][tc + 2] = (uint16_t)(w.y & 0xffffu);
@@ -242,38 +255,62 @@ __global__ __launch_bounds__(EW_THREADS) void apply_kernel(const MatDesc* __rest
 #pragma unroll
       for (int k = 0; k < 4; ++k) h[q][k] = T[tc + k][tr + 16 * q];
   }
+  if (write_w) {
+    MUON_GLOBAL float* W = gptr(d.W);
+    const bool vec = d.vec4 && (c0 + tc + 3 < d.cols);
+    float w[4][4];
+    // all loads of W first, then the stores
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int r = r0 + tr + 16 * q;
-    const int c = c0 + tc;
-    if (r >= d.rows) continue;
-    const int64_t off = (int64_t)r * d.cols + c;
-    if (write_w) {
-      if (d.vec4 && c + 3 < d.cols) {
-        float4 w = *reinterpret_cast<const float4*>(d.W + off);
-        w.x = w.x - lr * bf16_bits_to_f32(h[q][0]);
-        w.y = w.y - lr * bf16_bits_to_f32(h[q][1]);
-        w.z = w.z - lr * bf16_bits_to_f32(h[q][2]);
-        w.w = w.w - lr * bf16_bits_to_f32(h[q][3]);
-        *reinterpret_cast<float4*>(d.W + off) = w;
+    for (int q = 0; q < 4; ++q) {
+      const int r = r0 + tr + 16 * q;
+      const int64_t off = (int64_t)r * d.cols + c0 + tc;
+      if (r >= d.rows) continue;
+      if (vec) {
+        const f32x4 t = *reinterpret_cast<const MUON_GLOBAL f32x4*>(W + off);
+        w[q][0] = t.x; w[q][1] = t.y; w[q][2] = t.z; w[q][3] = t.w;
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) w[q][k] = (c0 + tc + k < d.cols) ? W[off + k] : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = r0 + tr + 16 * q;
+      const int64_t off = (int64_t)r * d.cols + c0 + tc;
+      if (r >= d.rows) continue;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) w[q][k] = w[q][k] - lr * bf16_bits_to_f32(h[q][k]);
+      if (vec) {
+        *reinterpret_cast<MUON_GLOBAL f32x4*>(W + off) = f32x4{w[q][0], w[q][1], w[q][2], w[q][3]};
       } else {
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-          if (c + k < d.cols) d.W[off + k] = d.W[off + k] - lr * bf16_bits_to_f32(h[q][k]);
+          if (c0 + tc + k < d.cols) W[off + k] = w[q][k];
       }
     }
-    if (d.upd) {
+  }
+  if (d.upd) {
+    MUON_GLOBAL uint16_t* U = gptr(d.upd);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = r0 + tr + 16 * q;
+      const int c = c0 + tc;
+      if (r >= d.rows) continue;
+      const int64_t off = (int64_t)r * d.cols + c;
 #pragma unroll
       for (int k = 0; k < 4; ++k)
-        if (c + k < d.cols) d.upd[off + k] = (uint16_t)h[q][k];
+        if (c + k < d.cols) U[off + k] = (uint16_t)h[q][k];
     }
   }
 }
 
-hipError_t launch_momentum(const MatDesc* d, const EwItem* items, int n_items, float beta,
+hipError_t launch_momentum(const MatDesc* d, const EwItem* items, int n_items, int n_mats, float beta,
                            hipStream_t s) {
   if (n_items == 0) return hipSuccess;
   momentum_kernel<<<n_items, EW_THREADS, 0, s>>>(d, items, beta);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  norm_finalize_kernel<<<n_mats, EW_THREADS, 0, s>>>(d);
   return hipGetLastError();
 }
 

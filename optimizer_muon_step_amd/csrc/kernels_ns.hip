@@ -58,17 +58,18 @@ __global__ __launch_bounds__(NS_THREADS, 2) void ns_gemm_kernel(const MatDesc* _
   __shared__ u32x4 lds[2][2][STAGE_CHUNKS];  // [stage][operand][chunk], 64 KB
 
   const GemmItem it = items[blockIdx.x];
+  if (it.mat < 0) return;  // padding item of a shorter per-XCD run
   const MatDesc& d = descs[it.mat];
-  const uint16_t* __restrict__ Aop;
-  const uint16_t* __restrict__ Bop;
-  uint16_t* __restrict__ C;
+  const MUON_GLOBAL uint16_t* Aop;
+  const MUON_GLOBAL uint16_t* Bop;
+  MUON_GLOBAL uint16_t* C;
   int lda, ldb, ldc, K;
   if (KIND == GEMM_GRAM) {
-    Aop = d.X[src]; Bop = d.X[src]; lda = ldb = d.n_pad; K = d.n_pad; C = d.A; ldc = d.m_pad;
+    Aop = gptr(d.X[src]); Bop = Aop; lda = ldb = d.n_pad; K = d.n_pad; C = gptr(d.A); ldc = d.m_pad;
   } else if (KIND == GEMM_POLY) {
-    Aop = d.A; Bop = d.A; lda = ldb = d.m_pad; K = d.m_pad; C = d.B; ldc = d.m_pad;
+    Aop = gptr(d.A); Bop = Aop; lda = ldb = d.m_pad; K = d.m_pad; C = gptr(d.B); ldc = d.m_pad;
   } else {
-    Aop = d.B; lda = d.m_pad; Bop = d.X[src]; ldb = d.n_pad; K = d.m_pad; C = d.X[src ^ 1];
+    Aop = gptr(d.B); lda = d.m_pad; Bop = gptr(d.X[src]); ldb = d.n_pad; K = d.m_pad; C = gptr(d.X[src ^ 1]);
     ldc = d.n_pad;
   }
   const int row0 = it.ti * TILE;  // output rows   (rows of Aop)
@@ -85,21 +86,21 @@ __global__ __launch_bounds__(NS_THREADS, 2) void ns_gemm_kernel(const MatDesc* _
     for (int q = 0; q < 4; ++q) {
       const int c = tid + NS_THREADS * q;
       const int row = c >> 3, ch = c & 7;
-      ra[q] = *reinterpret_cast<const u32x4*>(Aop + (int64_t)(row0 + row) * lda + k0 + ch * 8);
+      ra[q] = *reinterpret_cast<const MUON_GLOBAL u32x4*>(Aop + (int64_t)(row0 + row) * lda + k0 + ch * 8);
     }
     if (KIND != GEMM_UPDATE) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int c = tid + NS_THREADS * q;
         const int row = c >> 3, ch = c & 7;
-        rb[q] = *reinterpret_cast<const u32x4*>(Bop + (int64_t)(col0 + row) * ldb + k0 + ch * 8);
+        rb[q] = *reinterpret_cast<const MUON_GLOBAL u32x4*>(Bop + (int64_t)(col0 + row) * ldb + k0 + ch * 8);
       }
     } else {
       // X tile: k rows k0 + 4kq .. +3, columns col0 + 8jb .. +7
       const int jb = tid & 15, kq = tid >> 4;
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        rb[r] = *reinterpret_cast<const u32x4*>(Bop + (int64_t)(k0 + 4 * kq + r) * ldb + col0 + 8 * jb);
+        rb[r] = *reinterpret_cast<const MUON_GLOBAL u32x4*>(Bop + (int64_t)(k0 + 4 * kq + r) * ldb + col0 + 8 * jb);
     }
   };
   auto sstore = [&](int stage) {
@@ -140,28 +141,48 @@ __global__ __launch_bounds__(NS_THREADS, 2) void ns_gemm_kernel(const MatDesc* _
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[mi][nj][e] = 0.0f;
 
+  // Fragments for k-step kk+1 are read from LDS while the MFMAs of k-step kk run.
+  auto read_frags = [&](int stage, int kk, bf16x8* af, bf16x8* bfr) {
+    const int ch = 2 * kk + (lane >> 5);
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+      af[mi] = __builtin_bit_cast(bf16x8, lds[stage][0][swz(wi * 64 + mi * 32 + (lane & 31), ch)]);
+#pragma unroll
+    for (int nj = 0; nj < 2; ++nj)
+      bfr[nj] = __builtin_bit_cast(bf16x8, lds[stage][1][swz(wj * 64 + nj * 32 + (lane & 31), ch)]);
+  };
   auto compute = [&](int stage) {
+    bf16x8 af[2][2], bfr[2][2];
+    read_frags(stage, 0, af[0], bfr[0]);
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
-      const int ch = 2 * kk + (lane >> 5);
-      bf16x8 af[2], bfr[2];
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi) {
-        const int r = wi * 64 + mi * 32 + (lane & 31);
-        af[mi] = __builtin_bit_cast(bf16x8, lds[stage][0][swz(r, ch)]);
-      }
-#pragma unroll
-      for (int nj = 0; nj < 2; ++nj) {
-        const int r = wj * 64 + nj * 32 + (lane & 31);
-        bfr[nj] = __builtin_bit_cast(bf16x8, lds[stage][1][swz(r, ch)]);
-      }
+      if (kk + 1 < BK / 16) read_frags(stage, kk + 1, af[(kk + 1) & 1], bfr[(kk + 1) & 1]);
       // operands swapped so each lane ends up with 4 consecutive output columns
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
         for (int nj = 0; nj < 2; ++nj)
-          acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[nj], af[mi], acc[mi][nj], 0, 0, 0);
+          acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[kk & 1][nj], af[kk & 1][mi], acc[mi][nj], 0, 0, 0);
     }
+  };
+
+  // Epilogue inputs (A for POLY, X for UPDATE) at the positions this lane
+  // owns; fetched during the last K step so their latency is hidden.
+  u32x2 ein[2][2][4];
+  auto eload = [&]() {
+    if (KIND == GEMM_GRAM) return;
+    const MUON_GLOBAL uint16_t* E = (KIND == GEMM_POLY) ? gptr(d.A) : gptr(d.X[src]);
+    const int lde = (KIND == GEMM_POLY) ? d.m_pad : d.n_pad;
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int nj = 0; nj < 2; ++nj)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const int i = row0 + wi * 64 + mi * 32 + (lane & 31);
+          const int j = col0 + wj * 64 + nj * 32 + 8 * e4 + 4 * (lane >> 5);
+          ein[mi][nj][e4] = *reinterpret_cast<const MUON_GLOBAL u32x2*>(E + (int64_t)i * lde + j);
+        }
   };
 
   const int KT = K / BK;
@@ -170,7 +191,10 @@ __global__ __launch_bounds__(NS_THREADS, 2) void ns_gemm_kernel(const MatDesc* _
   __syncthreads();
   for (int kt = 0; kt < KT; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < KT) gload((kt + 1) * BK);
+    if (kt + 1 < KT)
+      gload((kt + 1) * BK);
+    else
+      eload();
     compute(cur);
     if (kt + 1 < KT) sstore(cur ^ 1);
     __syncthreads();
@@ -190,16 +214,11 @@ __global__ __launch_bounds__(NS_THREADS, 2) void ns_gemm_kernel(const MatDesc* _
         float v[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) v[k] = acc[mi][nj][4 * e4 + k];
-        if (KIND == GEMM_POLY) {
-          const u32x2 a2 = *reinterpret_cast<const u32x2*>(d.A + (int64_t)i * d.m_pad + j);
-          const float av[4] = {bf16_lo(a2.x), bf16_hi(a2.x), bf16_lo(a2.y), bf16_hi(a2.y)};
+        if (KIND != GEMM_GRAM) {
+          const u32x2 e2 = ein[mi][nj][e4];
+          const float ev[4] = {bf16_lo(e2.x), bf16_hi(e2.x), bf16_lo(e2.y), bf16_hi(e2.y)};
 #pragma unroll
-          for (int k = 0; k < 4; ++k) v[k] = cb * av[k] + cc * v[k];
-        } else if (KIND == GEMM_UPDATE) {
-          const u32x2 x2 = *reinterpret_cast<const u32x2*>(d.X[src] + (int64_t)i * d.n_pad + j);
-          const float xv[4] = {bf16_lo(x2.x), bf16_hi(x2.x), bf16_lo(x2.y), bf16_hi(x2.y)};
-#pragma unroll
-          for (int k = 0; k < 4; ++k) v[k] = ca * xv[k] + v[k];
+          for (int k = 0; k < 4; ++k) v[k] = (KIND == GEMM_POLY) ? cb * ev[k] + cc * v[k] : ca * ev[k] + v[k];
         }
         uint32_t h[4];
 #pragma unroll
@@ -208,7 +227,7 @@ __global__ __launch_bounds__(NS_THREADS, 2) void ns_gemm_kernel(const MatDesc* _
           u32x2 o;
           o.x = h[0] | (h[1] << 16);
           o.y = h[2] | (h[3] << 16);
-          *reinterpret_cast<u32x2*>(C + (int64_t)i * ldc + j) = o;
+          *reinterpret_cast<MUON_GLOBAL u32x2*>(C + (int64_t)i * ldc + j) = o;
           if (KIND != GEMM_UPDATE) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) C[(int64_t)(j + k) * ldc + i] = (uint16_t)h[k];

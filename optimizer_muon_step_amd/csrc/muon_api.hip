@@ -44,12 +44,10 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v, size_t a = kAlign) { return (v + a - 1) / a * a; }
 int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
-// Control region at the start of every workspace: one completion counter and
-// one scale per matrix slot.  The counters are zeroed when a workspace is
-// acquired and every call leaves them at zero again.
-constexpr size_t kCounterBytes = sizeof(uint32_t) * MUON_MAX_MATRICES;
+// Control region at the start of every workspace: one normalisation scale per
+// matrix slot.
 constexpr size_t kScaleBytes = sizeof(float) * MUON_MAX_MATRICES;
-constexpr size_t kControlBytes = kCounterBytes + kScaleBytes;
+constexpr size_t kControlBytes = kScaleBytes;
 
 struct Geometry {
   int32_t rows, cols, m, n, m_pad, n_pad, transposed, part_cnt;
@@ -134,9 +132,10 @@ struct Plan {
   EwItem* d_mom = nullptr;
   EwItem* d_cast = nullptr;
   EwItem* d_apply = nullptr;
-  GemmItem* d_sym = nullptr;
+  GemmItem* d_gram = nullptr;
+  GemmItem* d_poly = nullptr;
   GemmItem* d_upd = nullptr;
-  int n_mom = 0, n_cast = 0, n_apply = 0, n_sym = 0, n_upd = 0;
+  int n_mom = 0, n_cast = 0, n_apply = 0, n_gram = 0, n_poly = 0, n_upd = 0;
   ~Plan() {
     if (dev) (void)hipFree(dev);
     if (host) (void)hipHostFree(host);
@@ -191,16 +190,36 @@ int acquire_workspace(DeviceState& st, size_t need, hipStream_t stream) {
       return fail(MUON_ENOMEM, "hipMalloc of %zu workspace bytes failed: %s", want, hipGetErrorString(e));
     }
   }
-  // Counters start at zero; wait so that a later call on another stream sees it.
-  if ((e = hipMemsetAsync(p, 0, kCounterBytes, stream)) != hipSuccess ||
-      (e = hipStreamSynchronize(stream)) != hipSuccess) {
-    (void)hipFree(p);
-    return fail_hip(e, "workspace counter reset");
-  }
   st.ws = p;
   st.ws_bytes = want;
   st.ws_owned = true;
   return MUON_OK;
+}
+
+// Workgroup w of a launch runs on XCD w % kXcds, and each XCD has its own L2.
+// Cut the locality-ordered tile sequence into kXcds contiguous runs of about
+// equal cost and interleave them, so that each XCD works through one run and
+// its concurrently resident tiles share operands in that XCD's L2.  Runs of
+// unequal length are padded with empty items (mat = -1) that exit at once.
+constexpr int kXcds = 8;
+
+std::vector<GemmItem> xcd_interleave(const std::vector<GemmItem>& seq, const std::vector<int64_t>& cost) {
+  int64_t total = 0;
+  for (int64_t c : cost) total += c;
+  std::vector<std::vector<GemmItem>> run(kXcds);
+  int64_t acc = 0;
+  int x = 0;
+  for (size_t k = 0; k < seq.size(); ++k) {
+    while (x < kXcds - 1 && acc >= total * (x + 1) / kXcds) ++x;
+    run[x].push_back(seq[k]);
+    acc += cost[k];
+  }
+  size_t len = 0;
+  for (auto& r : run) len = std::max(len, r.size());
+  std::vector<GemmItem> out(len * kXcds, GemmItem{-1, 0, 0});
+  for (int r = 0; r < kXcds; ++r)
+    for (size_t k = 0; k < run[r].size(); ++k) out[k * kXcds + r] = run[r][k];
+  return out;
 }
 
 template <typename T>
@@ -240,10 +259,9 @@ int get_plan(DeviceState& st, int mode, int n, const muon_shape_t* shapes, float
   plan->key = std::move(key);
   std::vector<MatDesc> desc(n);
   std::vector<EwItem> mom, cast, apply;
-  std::vector<GemmItem> sym, updl;
+  std::vector<GemmItem> gram, poly, updl;
   char* cur = static_cast<char*>(st.ws);
-  uint32_t* counters = reinterpret_cast<uint32_t*>(cur);
-  float* scales = reinterpret_cast<float*>(cur + kCounterBytes);
+  float* scales = reinterpret_cast<float*>(cur);
   cur += kControlBytes;
   for (int i = 0; i < n; ++i) {
     const Geometry g = geometry_of(shapes[i]);
@@ -260,7 +278,6 @@ int get_plan(DeviceState& st, int mode, int n, const muon_shape_t* shapes, float
     d.B = carve<uint16_t>(cur, g.a_bytes / 2);
     d.part = carve<double>(cur, g.part_bytes / sizeof(double));
     d.scale = scales + i;
-    d.counter = counters + i;
     d.rows = g.rows;
     d.cols = g.cols;
     d.m = g.m;
@@ -281,17 +298,29 @@ int get_plan(DeviceState& st, int mode, int n, const muon_shape_t* shapes, float
     const int at = ((g.rows + CAST_TILE - 1) / CAST_TILE) * ((g.cols + CAST_TILE - 1) / CAST_TILE);
     for (int t = 0; t < at; ++t) apply.push_back({i, t});
   }
-  // GEMM tiles, longest K first so the tail of each launch holds short tiles.
-  std::vector<int> order(n);
-  for (int i = 0; i < n; ++i) order[i] = i;
-  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return desc[a].n_pad > desc[b].n_pad; });
-  for (int i : order) {
+  // GEMM tiles.  Per matrix in an order that reuses operands (update: all row
+  // tiles of one column block in a row, sharing that block of X; symmetric
+  // phases: upper-triangle tiles row by row), then spread over the XCDs.
+  std::vector<GemmItem> gram_seq, upd_seq;
+  std::vector<int64_t> gram_cost, upd_cost;
+  for (int i = 0; i < n; ++i) {
     const int tm = desc[i].m_pad / NS_TILE, tn = desc[i].n_pad / NS_TILE;
     for (int ti = 0; ti < tm; ++ti)
-      for (int tj = ti; tj < tm; ++tj) sym.push_back({i, (int16_t)ti, (int16_t)tj});
-    for (int ti = 0; ti < tm; ++ti)
-      for (int tj = 0; tj < tn; ++tj) updl.push_back({i, (int16_t)ti, (int16_t)tj});
+      for (int tj = ti; tj < tm; ++tj) {
+        gram_seq.push_back({i, (int16_t)ti, (int16_t)tj});
+        gram_cost.push_back(desc[i].n_pad);
+      }
+    for (int tj = 0; tj < tn; ++tj)
+      for (int ti = 0; ti < tm; ++ti) {
+        upd_seq.push_back({i, (int16_t)ti, (int16_t)tj});
+        upd_cost.push_back(desc[i].m_pad);
+      }
   }
+  std::vector<int64_t> poly_cost(gram_seq.size());
+  for (size_t k = 0; k < gram_seq.size(); ++k) poly_cost[k] = desc[gram_seq[k].mat].m_pad;
+  gram = xcd_interleave(gram_seq, gram_cost);
+  poly = xcd_interleave(gram_seq, poly_cost);
+  updl = xcd_interleave(upd_seq, upd_cost);
 
   size_t off = 0;
   auto place = [&](size_t bytes) { const size_t o = off; off += align_up(bytes); return o; };
@@ -299,7 +328,8 @@ int get_plan(DeviceState& st, int mode, int n, const muon_shape_t* shapes, float
   const size_t o_mom = place(sizeof(EwItem) * mom.size());
   const size_t o_cast = place(sizeof(EwItem) * cast.size());
   const size_t o_apply = place(sizeof(EwItem) * apply.size());
-  const size_t o_sym = place(sizeof(GemmItem) * sym.size());
+  const size_t o_gram = place(sizeof(GemmItem) * gram.size());
+  const size_t o_poly = place(sizeof(GemmItem) * poly.size());
   const size_t o_upd = place(sizeof(GemmItem) * updl.size());
   plan->bytes = std::max<size_t>(off, kAlign);
   hipError_t e;
@@ -317,7 +347,8 @@ int get_plan(DeviceState& st, int mode, int n, const muon_shape_t* shapes, float
   memcpy(h + o_mom, mom.data(), sizeof(EwItem) * mom.size());
   memcpy(h + o_cast, cast.data(), sizeof(EwItem) * cast.size());
   memcpy(h + o_apply, apply.data(), sizeof(EwItem) * apply.size());
-  memcpy(h + o_sym, sym.data(), sizeof(GemmItem) * sym.size());
+  memcpy(h + o_gram, gram.data(), sizeof(GemmItem) * gram.size());
+  memcpy(h + o_poly, poly.data(), sizeof(GemmItem) * poly.size());
   memcpy(h + o_upd, updl.data(), sizeof(GemmItem) * updl.size());
   if ((e = hipMemcpyAsync(plan->dev, plan->host, plan->bytes, hipMemcpyHostToDevice, stream)) != hipSuccess)
     return fail_hip(e, "hipMemcpyAsync(plan)");
@@ -328,12 +359,14 @@ int get_plan(DeviceState& st, int mode, int n, const muon_shape_t* shapes, float
   plan->d_mom = reinterpret_cast<EwItem*>(dv + o_mom);
   plan->d_cast = reinterpret_cast<EwItem*>(dv + o_cast);
   plan->d_apply = reinterpret_cast<EwItem*>(dv + o_apply);
-  plan->d_sym = reinterpret_cast<GemmItem*>(dv + o_sym);
+  plan->d_gram = reinterpret_cast<GemmItem*>(dv + o_gram);
+  plan->d_poly = reinterpret_cast<GemmItem*>(dv + o_poly);
   plan->d_upd = reinterpret_cast<GemmItem*>(dv + o_upd);
   plan->n_mom = (int)mom.size();
   plan->n_cast = (int)cast.size();
   plan->n_apply = (int)apply.size();
-  plan->n_sym = (int)sym.size();
+  plan->n_gram = (int)gram.size();
+  plan->n_poly = (int)poly.size();
   plan->n_upd = (int)updl.size();
   st.plans.push_front(std::move(plan));
   while (st.plans.size() > kMaxPlans) st.plans.pop_back();
@@ -378,7 +411,7 @@ int run(int mode, float* const* params, const float* const* grads, float* const*
   if ((rc = get_plan(st, mode, n, shapes, params, grads, moms, upd, xin, stream, &p))) return rc;
   const float ca = coeffs[0], cb = coeffs[1], cc = coeffs[2];
   if (mode == MODE_STEP) {
-    rc = timed(MUON_KERNEL_MOMENTUM, stream, [&] { return launch_momentum(p->d_desc, p->d_mom, p->n_mom, beta, stream); },
+    rc = timed(MUON_KERNEL_MOMENTUM, stream, [&] { return launch_momentum(p->d_desc, p->d_mom, p->n_mom, n, beta, stream); },
                "momentum kernel launch");
     if (rc) return rc;
   }
@@ -389,11 +422,11 @@ int run(int mode, float* const* params, const float* const* grads, float* const*
   for (int k = 0; k < ns_steps; ++k) {
     const int src = k & 1;
     rc = timed(MUON_KERNEL_GRAM, stream,
-               [&] { return launch_gemm(GEMM_GRAM, p->d_desc, p->d_sym, p->n_sym, src, ca, cb, cc, stream); },
+               [&] { return launch_gemm(GEMM_GRAM, p->d_desc, p->d_gram, p->n_gram, src, ca, cb, cc, stream); },
                "gram kernel launch");
     if (rc) return rc;
     rc = timed(MUON_KERNEL_POLY, stream,
-               [&] { return launch_gemm(GEMM_POLY, p->d_desc, p->d_sym, p->n_sym, src, ca, cb, cc, stream); },
+               [&] { return launch_gemm(GEMM_POLY, p->d_desc, p->d_poly, p->n_poly, src, ca, cb, cc, stream); },
                "poly kernel launch");
     if (rc) return rc;
     rc = timed(MUON_KERNEL_UPDATE, stream,
@@ -497,10 +530,7 @@ int muon_set_workspace(void* dev_ptr, size_t bytes) {
   st.ws = dev_ptr;
   st.ws_bytes = bytes;
   st.ws_owned = false;
-  if (dev_ptr) {
-    if ((e = hipMemset(dev_ptr, 0, kCounterBytes)) != hipSuccess || (e = hipDeviceSynchronize()) != hipSuccess)
-      return fail_hip(e, "workspace counter reset");
-  } else {
+  if (!dev_ptr) {
     st.ws = nullptr;
     st.ws_bytes = 0;
   }

@@ -15,7 +15,7 @@ constexpr int NS_THREADS = 256;
 
 // Elementwise kernels.
 constexpr int EW_THREADS = 256;
-constexpr int MOM_CHUNK = 16384;  // elements per momentum work item
+constexpr int MOM_CHUNK = 8192;   // elements per momentum work item (8 float4 per thread)
 constexpr int CAST_TILE = 64;     // square tile for the cast / apply kernels
 
 // One matrix of a call, in device memory.
@@ -29,8 +29,7 @@ struct MatDesc {
   uint16_t* A;            // X X^T, m_pad x m_pad
   uint16_t* B;            // b A + c A A, m_pad x m_pad
   double* part;           // norm partial sums of this matrix (part_cnt of them)
-  float* scale;           // s = 1 / (||U||_F + eps), written by the momentum kernel
-  uint32_t* counter;      // finished momentum chunks; returns to 0 after each call
+  float* scale;           // s = 1 / (||U||_F + eps), written by norm_finalize_kernel
   int32_t rows, cols;     // caller orientation
   int32_t m, n;           // canonical, m <= n
   int32_t m_pad, n_pad;   // multiples of NS_TILE
@@ -55,7 +54,7 @@ struct EwItem {
 enum GemmKind { GEMM_GRAM = 0, GEMM_POLY = 1, GEMM_UPDATE = 2 };
 
 // ---- host launchers (kernels_*.hip) ----
-hipError_t launch_momentum(const MatDesc* d, const EwItem* items, int n_items, float beta,
+hipError_t launch_momentum(const MatDesc* d, const EwItem* items, int n_items, int n_mats, float beta,
                            hipStream_t s);
 hipError_t launch_cast(const MatDesc* d, const EwItem* items, int n_items, float beta, int from_bf16,
                        hipStream_t s);
