@@ -61,8 +61,8 @@ Geometry geometry_of(const muon_shape_t& s) {
   g.transposed = s.rows > s.cols;
   g.m = (int32_t)std::min(s.rows, s.cols);
   g.n = (int32_t)std::max(s.rows, s.cols);
-  g.m_pad = (int32_t)round_up(g.m, NS_TILE);
-  g.n_pad = (int32_t)round_up(g.n, NS_TILE);
+  g.m_pad = (int32_t)round_up(g.m, NS_PAD_M);
+  g.n_pad = (int32_t)round_up(g.n, NS_PAD_N);
   g.part_cnt = (int32_t)((s.rows * s.cols + MOM_CHUNK - 1) / MOM_CHUNK);
   g.x_bytes = align_up((size_t)g.m_pad * g.n_pad * 2);
   g.a_bytes = align_up((size_t)g.m_pad * g.m_pad * 2);
@@ -304,14 +304,14 @@ int get_plan(DeviceState& st, int mode, int n, const muon_shape_t* shapes, float
   std::vector<GemmItem> gram_seq, upd_seq;
   std::vector<int64_t> gram_cost, upd_cost;
   for (int i = 0; i < n; ++i) {
-    const int tm = desc[i].m_pad / NS_TILE, tn = desc[i].n_pad / NS_TILE;
+    const int tm = desc[i].m_pad / SYM_BM, tn = desc[i].n_pad / UPD_BN;
     for (int ti = 0; ti < tm; ++ti)
       for (int tj = ti; tj < tm; ++tj) {
         gram_seq.push_back({i, (int16_t)ti, (int16_t)tj});
         gram_cost.push_back(desc[i].n_pad);
       }
     for (int tj = 0; tj < tn; ++tj)
-      for (int ti = 0; ti < tm; ++ti) {
+      for (int ti = 0; ti < desc[i].m_pad / UPD_BM; ++ti) {
         upd_seq.push_back({i, (int16_t)ti, (int16_t)tj});
         upd_cost.push_back(desc[i].m_pad);
       }

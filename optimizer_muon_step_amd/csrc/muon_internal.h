@@ -6,11 +6,13 @@
 
 namespace muon {
 
-// Tile geometry of the Newton-Schulz GEMMs.  Every canonical dimension is
-// padded up to NS_TILE inside the workspace, with the padding held at exact
-// zero, so the GEMM kernels never bounds-check.
-constexpr int NS_TILE = 128;  // output tile edge (rows and columns)
-constexpr int NS_BK = 64;     // K slice staged through LDS per pipeline step
+// Tile geometry of the Newton-Schulz GEMMs.  Inside the workspace the
+// canonical m is padded to NS_PAD_M and n to NS_PAD_N, with the padding held
+// at exact zero, so the GEMM kernels never bounds-check.
+constexpr int SYM_BM = 128, SYM_BN = 128;  // GRAM / POLY output tile
+constexpr int UPD_BM = 128, UPD_BN = 256;  // UPDATE output tile
+constexpr int NS_PAD_M = 128;              // multiple of SYM_BM, SYM_BN, UPD_BM
+constexpr int NS_PAD_N = 256;              // multiple of UPD_BN
 constexpr int NS_THREADS = 256;
 
 // Elementwise kernels.
@@ -32,7 +34,7 @@ struct MatDesc {
   float* scale;           // s = 1 / (||U||_F + eps), written by norm_finalize_kernel
   int32_t rows, cols;     // caller orientation
   int32_t m, n;           // canonical, m <= n
-  int32_t m_pad, n_pad;   // multiples of NS_TILE
+  int32_t m_pad, n_pad;   // multiples of NS_PAD_M / NS_PAD_N
   int32_t transposed;     // 1 when rows > cols
   int32_t part_cnt;
   int32_t vec4;           // 1 when every row start allows 4-element vector access
@@ -42,7 +44,7 @@ struct MatDesc {
 // GEMM work item: one output tile of one matrix.
 struct GemmItem {
   int32_t mat;
-  int16_t ti, tj;  // tile row / column in units of NS_TILE
+  int16_t ti, tj;  // tile row / column in units of the launch's tile shape
 };
 
 // Elementwise work item: chunk (momentum) or tile (cast / apply) of a matrix.
