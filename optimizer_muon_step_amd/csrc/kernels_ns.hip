@@ -12,18 +12,17 @@
 // combinations are plain fp32 products and sums (no fused multiply-add) and
 // every stored value is rounded to bf16, nearest-even.
 //
-// Pipeline: 256 threads = 4 waves in a 2x2 grid over a BM x BN output tile.
-// K advances in slices of 32 through a ring of NSTAGE LDS buffers filled by
-// global_load_lds_dwordx4 (global memory straight into LDS, no registers), so
-// NSTAGE-1 slices are in flight while one is multiplied.  Each lane's 16-byte
-// DMA slot is fixed by its lane id; the XOR swizzle of a tile is therefore
-// applied on the global side (each lane fetches the chunk that belongs in its
-// slot).  k-contiguous tiles (X for GRAM, A for POLY, B for UPDATE) feed MFMA
-// fragments with ds_read_b128; the k-major X tile of UPDATE is read with
-// ds_read_b64_tr_b16 (see read_tr_frags), which transposes 16-bit elements across each group of
-// 16 lanes: with lane L of a group addressing row k0 + L/4, columns
-// j0 + 4(L%4) .. +3, lane i of the group receives column j0 + i, rows
-// k0 .. k0+3.
+// Pipeline: WAVES_M x WAVES_N waves over a BM x BN output tile.  K advances in
+// slices of 64 through a ring of NSTAGE LDS buffers filled by
+// global_load_lds_dwordx4 (global memory straight into LDS, no registers):
+// NSTAGE-1 slices are in flight while one is multiplied, and every row
+// segment fetched is a whole 128-byte line.  Each lane's 16-byte DMA slot is
+// fixed by its lane id, so a tile's XOR swizzle is applied on the global side
+// (each lane fetches the chunk that belongs in its slot).  k-contiguous tiles
+// (X for GRAM, A for POLY, B for UPDATE) feed MFMA fragments with
+// ds_read_b128; the k-major X tile of UPDATE is read with ds_read_b64_tr_b16
+// (see read_tr_frags).  The swizzles assume gfx950's LDS of 64 four-byte
+// banks.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -40,76 +39,72 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #define LDS_AS __attribute__((address_space(3)))
 
-constexpr int BK = 32;  // K per pipeline stage: 4 chunks of 16 B per k-contiguous row
+constexpr int BK = 64;  // K per pipeline stage: one 128-byte line per k-contiguous row
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] + vmcnt_hi[15:14],
 // expcnt[6:4], lgkmcnt[11:8]): wait until at most n vector-memory operations
 // are outstanding and every LDS operation has completed.
 constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (0 << 8); }
 
-// Swizzled 16-byte chunk of a k-contiguous row (4 chunks per row): rows r and
-// r+1 share a 128-byte bank line, so XOR by (r/2)%4 gives eight consecutive
-// rows eight distinct bank groups.
-__device__ __forceinline__ int swz_k(int row, int chunk) { return chunk ^ ((row >> 1) & 3); }
-// Swizzled chunk of a k-major row (BN/8 chunks per row): the transposing
-// read touches 4 consecutive rows at the same columns; XOR by 2(r%4) puts
-// them in four different 32-byte bank groups.
-__device__ __forceinline__ int swz_n(int row, int chunk) { return chunk ^ (2 * (row & 3)); }
-
 template <int n>
 __device__ __forceinline__ void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(n));
 }
 
-// B fragments of one k-step from a k-major LDS tile: 2 x TN transposing
-// reads.  They are issued from inline assembly because the compiler would
-// otherwise wait for every in-flight global->LDS transfer (including later
-// pipeline stages) before each such read.  The block ends with its own wait,
-// so every output is complete when the block retires; outputs are
-// early-clobber so no output register aliases an address input.
-template <int TN>
-__device__ __forceinline__ void read_tr_frags(bf16x8* bfr, const LDS_AS char* st, const int (*b_rd)[2][2],
-                                              int kk) {
-  static_assert(TN == 4, "read_tr_frags is written for four 32-column fragments");
-  uint64_t r[8];
-  const uint32_t base = (uint32_t)(uintptr_t)st;
+// k-contiguous tile: rows of 128 B (8 chunks of 16 B).  A fragment read has
+// 16 lanes on 16 consecutive rows at one chunk; two rows share a 256-byte
+// bank line, so XOR by (r/2)%8 sends the 16 reads to 16 distinct chunks.
+__device__ __forceinline__ int swz_k(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+// k-major tile: rows of BN*2 bytes.  A transposing read has each 16-lane
+// group on 4 consecutive rows, 32 bytes each, and pairs of groups 32 bytes
+// apart; XOR by 4(r%4) moves the 4 rows into different 64-byte bank groups.
+__device__ __forceinline__ int swz_n(int row, int chunk) { return chunk ^ (4 * (row & 3)); }
+
+// B fragments of one k-step from a k-major LDS tile: two transposing reads
+// per 32-column fragment (ds_read_b64_tr_b16 transposes 16-bit elements
+// across each group of 16 lanes: with lane L of a group addressing row
+// k0 + L/4, columns j0 + 4(L%4) .. +3, lane i of the group receives column
+// j0 + i, rows k0 .. k0+3).  They are issued from inline assembly because the
+// compiler would otherwise wait for every in-flight global->LDS transfer,
+// later pipeline stages included, before each such read.  The block ends with
+// its own wait, so every output is complete when the block retires; outputs
+// are early-clobber so no output register aliases an address input.
+__device__ __forceinline__ void read_tr_frags2(bf16x8* bfr, uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3) {
+  uint64_t r0, r1, r2, r3;
   asm volatile(
-      "ds_read_b64_tr_b16 %0, %8\n\t"
-      "ds_read_b64_tr_b16 %1, %9\n\t"
-      "ds_read_b64_tr_b16 %2, %10\n\t"
-      "ds_read_b64_tr_b16 %3, %11\n\t"
-      "ds_read_b64_tr_b16 %4, %12\n\t"
-      "ds_read_b64_tr_b16 %5, %13\n\t"
-      "ds_read_b64_tr_b16 %6, %14\n\t"
-      "ds_read_b64_tr_b16 %7, %15\n\t"
+      "ds_read_b64_tr_b16 %0, %4\n\t"
+      "ds_read_b64_tr_b16 %1, %5\n\t"
+      "ds_read_b64_tr_b16 %2, %6\n\t"
+      "ds_read_b64_tr_b16 %3, %7\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
-      : "v"(base + b_rd[0][kk][0]), "v"(base + b_rd[0][kk][1]), "v"(base + b_rd[1][kk][0]),
-        "v"(base + b_rd[1][kk][1]), "v"(base + b_rd[2][kk][0]), "v"(base + b_rd[2][kk][1]),
-        "v"(base + b_rd[3][kk][0]), "v"(base + b_rd[3][kk][1])
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
       : "memory");
-#pragma unroll
-  for (int nj = 0; nj < 4; ++nj)
-    bfr[nj] = __builtin_bit_cast(bf16x8, u32x4{(uint32_t)r[2 * nj], (uint32_t)(r[2 * nj] >> 32),
-                                               (uint32_t)r[2 * nj + 1], (uint32_t)(r[2 * nj + 1] >> 32)});
+  bfr[0] = __builtin_bit_cast(bf16x8, u32x4{(uint32_t)r0, (uint32_t)(r0 >> 32), (uint32_t)r1, (uint32_t)(r1 >> 32)});
+  bfr[1] = __builtin_bit_cast(bf16x8, u32x4{(uint32_t)r2, (uint32_t)(r2 >> 32), (uint32_t)r3, (uint32_t)(r3 >> 32)});
 }
 
 }  // namespace
 
-template <int KIND, int BM, int BN, int NSTAGE>
-__global__ __launch_bounds__(NS_THREADS, 2) void ns_gemm_kernel(const MatDesc* __restrict__ descs,
-                                                               const GemmItem* __restrict__ items,
-                                                               int src, float ca, float cb, float cc) {
-  constexpr bool NN = (KIND == GEMM_UPDATE);  // B operand stored k-major
-  constexpr int TM = BM / 64, TN = BN / 64;   // 32x32 MFMA tiles per wave (2x2 waves)
+template <int KIND, int BM, int BN, int WAVES_M, int WAVES_N, int NSTAGE>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const MatDesc* __restrict__ descs,
+                                                                        const GemmItem* __restrict__ items,
+                                                                        int src, float ca, float cb, float cc) {
+  constexpr int NT = 64 * WAVES_M * WAVES_N;   // threads
+  constexpr bool NN = (KIND == GEMM_UPDATE);   // B operand stored k-major
+  constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;  // wave tile
+  constexpr int TM = WTM / 32, TN = WTN / 32;            // 32x32 MFMA tiles per wave
   constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
   constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-  constexpr int A_INSTR = A_BYTES / (16 * NS_THREADS);  // DMA instructions per wave per stage
-  constexpr int B_INSTR = B_BYTES / (16 * NS_THREADS);
+  constexpr int A_INSTR = A_BYTES / (16 * NT);  // DMA instructions per wave per stage
+  constexpr int B_INSTR = B_BYTES / (16 * NT);
   constexpr int LPW = A_INSTR + B_INSTR;
   constexpr int NCHUNK_N = BN / 8;  // chunks per k-major row
-  static_assert(A_INSTR >= 1 && B_INSTR >= 1 && NSTAGE >= 2 && NSTAGE <= 4, "unsupported tile");
-  static_assert(NS_THREADS == 256, "2x2 waves");
+  static_assert(A_INSTR >= 1 && B_INSTR >= 1 && A_INSTR * 16 * NT == A_BYTES && B_INSTR * 16 * NT == B_BYTES,
+                "tile does not split into whole DMA instructions");
+  static_assert(NSTAGE >= 2 && NSTAGE <= 3 && TM >= 1 && TN >= 1, "unsupported tile");
+  static_assert(!NN || TN == 2, "the transposing read path is written for two fragments per wave");
+  static_assert(!NN || BN >= 128, "k-major swizzle needs 16 chunks per row");
   __shared__ __attribute__((aligned(16))) char lds[NSTAGE * STAGE_BYTES];
 
   const GemmItem it = items[blockIdx.x];
@@ -127,28 +122,32 @@ __global__ __launch_bounds__(NS_THREADS, 2) void ns_gemm_kernel(const MatDesc* _
     Aop = d.B; lda = d.m_pad; Bop = d.X[src]; ldb = d.n_pad; K = d.m_pad; C = gptr(d.X[src ^ 1]);
     ldc = d.n_pad;
   }
-  const int row0 = it.ti * BM;  // output rows    (rows of Aop)
-  const int col0 = it.tj * BN;  // output columns (rows of Bop for GRAM/POLY, columns of X for UPDATE)
+  // Output rows are rows of Aop; tile rows are counted in units of 128 so a
+  // BM = 256 tile may hang over the last 128-row block of m_pad.  Such rows
+  // load a clamped (valid) row, compute values that are never stored.
+  const int row0 = it.ti * 128;
+  const int col0 = it.tj * BN;  // output columns: rows of Bop (GRAM/POLY), columns of X (UPDATE)
+  const int row_lim = d.m_pad;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wi = wave >> 1, wj = wave & 1;
+  const int wi = wave / WAVES_N, wj = wave % WAVES_N;
 
   // Per-lane global source of each DMA instruction at k = 0 (element offsets).
   int64_t a_off[A_INSTR], b_off[B_INSTR];
 #pragma unroll
   for (int q = 0; q < A_INSTR; ++q) {
     const int s = (wave * A_INSTR + q) * 64 + lane;
-    const int row = s >> 2;
-    a_off[q] = (int64_t)(row0 + row) * lda + swz_k(row, s & 3) * 8;
+    const int row = s >> 3;
+    a_off[q] = (int64_t)min(row0 + row, row_lim - 1) * lda + swz_k(row, s & 7) * 8;
   }
 #pragma unroll
   for (int q = 0; q < B_INSTR; ++q) {
     const int s = (wave * B_INSTR + q) * 64 + lane;
     if (!NN) {
-      const int row = s >> 2;
-      b_off[q] = (int64_t)(col0 + row) * ldb + swz_k(row, s & 3) * 8;
+      const int row = s >> 3;
+      b_off[q] = (int64_t)(col0 + row) * ldb + swz_k(row, s & 7) * 8;
     } else {
       const int row = s / NCHUNK_N;
       b_off[q] = (int64_t)row * ldb + col0 + swz_n(row, s % NCHUNK_N) * 8;
@@ -176,48 +175,50 @@ __global__ __launch_bounds__(NS_THREADS, 2) void ns_gemm_kernel(const MatDesc* _
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[mi][nj][e] = 0.0f;
 
-  // LDS byte offsets (within a stage) of this lane's fragment reads.
-  int a_rd[TM][2], b_rd[TN][2][2];
+  // LDS byte offsets (within a stage) of this lane's fragment reads at k-step
+  // 0 of a stage: chunk lane/32 of each k-contiguous row.
+  int a_rd[TM], b_rd[TN][2];
 #pragma unroll
-  for (int mi = 0; mi < TM; ++mi)
+  for (int mi = 0; mi < TM; ++mi) {
+    const int r = wi * WTM + mi * 32 + (lane & 31);
+    a_rd[mi] = r * 128 + swz_k(r, lane >> 5) * 16;
+  }
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int r = wi * (BM / 2) + mi * 32 + (lane & 31);
-      a_rd[mi][kk] = r * 64 + swz_k(r, 2 * kk + (lane >> 5)) * 16;
-    }
+  for (int nj = 0; nj < TN; ++nj) {
+    if (!NN) {
+      const int r = wj * WTN + nj * 32 + (lane & 31);
+      b_rd[nj][0] = A_BYTES + r * 128 + swz_k(r, lane >> 5) * 16;
+      b_rd[nj][1] = 0;
+    } else {
+      const int g = (lane >> 4) & 3, l16 = lane & 15;
 #pragma unroll
-  for (int nj = 0; nj < TN; ++nj)
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      if (!NN) {
-        const int r = wj * (BN / 2) + nj * 32 + (lane & 31);
-        b_rd[nj][kk][0] = A_BYTES + r * 64 + swz_k(r, 2 * kk + (lane >> 5)) * 16;
-        b_rd[nj][kk][1] = 0;
-      } else {
-        const int g = (lane >> 4) & 3, l16 = lane & 15;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int k = 16 * kk + 8 * (g >> 1) + 4 * h + (l16 >> 2);
-          const int j = wj * (BN / 2) + nj * 32 + 16 * (g & 1) + 4 * (l16 & 3);
-          b_rd[nj][kk][h] = A_BYTES + k * (BN * 2) + swz_n(k, j >> 3) * 16 + (j & 7) * 2;
-        }
+      for (int h = 0; h < 2; ++h) {
+        const int k = 8 * (g >> 1) + 4 * h + (l16 >> 2);
+        const int j = wj * WTN + nj * 32 + 16 * (g & 1) + 4 * (l16 & 3);
+        b_rd[nj][h] = A_BYTES + k * (BN * 2) + swz_n(k, j >> 3) * 16 + (j & 7) * 2;
       }
     }
+  }
 
   auto compute = [&](int kt) {
     const LDS_AS char* st = (const LDS_AS char*)lds + (kt % NSTAGE) * STAGE_BYTES;
+    const uint32_t st_addr = (uint32_t)(uintptr_t)st;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < BK / 16; ++kk) {
       bf16x8 af[TM], bfr[TN];
+      // k-step kk reads logical chunk 2kk + lane/32; the swizzle is an XOR, so
+      // that is the k-step-0 chunk XOR 2kk, i.e. the byte offset XOR 32kk.
 #pragma unroll
       for (int mi = 0; mi < TM; ++mi)
-        af[mi] = __builtin_bit_cast(bf16x8, *(const LDS_AS u32x4*)(st + a_rd[mi][kk]));
+        af[mi] = __builtin_bit_cast(bf16x8, *(const LDS_AS u32x4*)(st + (a_rd[mi] ^ (32 * kk))));
       if constexpr (!NN) {
 #pragma unroll
         for (int nj = 0; nj < TN; ++nj)
-          bfr[nj] = __builtin_bit_cast(bf16x8, *(const LDS_AS u32x4*)(st + b_rd[nj][kk][0]));
+          bfr[nj] = __builtin_bit_cast(bf16x8, *(const LDS_AS u32x4*)(st + (b_rd[nj][0] ^ (32 * kk))));
       } else {
-        read_tr_frags<TN>(bfr, st, b_rd, kk);
+        // k-step kk is 16 rows further on; (row % 4), hence the swizzle, is unchanged
+        const uint32_t dk = st_addr + kk * 16 * (BN * 2);
+        read_tr_frags2(bfr, dk + b_rd[0][0], dk + b_rd[0][1], dk + b_rd[1][0], dk + b_rd[1][1]);
       }
       // operands swapped so each lane ends up with 4 consecutive output columns
 #pragma unroll
@@ -228,23 +229,34 @@ __global__ __launch_bounds__(NS_THREADS, 2) void ns_gemm_kernel(const MatDesc* _
     }
   };
 
-  // Epilogue inputs (A for POLY, X for UPDATE) at the positions this lane
-  // owns; fetched during the last K step so their latency is hidden.
+  // POLY's b*A term needs A[i][j], which is column k = j of the staged A tile:
+  // it is read out of the K slice that holds it (no extra global traffic).
+  // UPDATE's a*X term is fetched into LDS after the main loop instead
+  // (holding it in registers through the loop would exceed the budget).
   u32x2 ein[TM][TN][4];
-  auto eload = [&]() {
-    if (KIND == GEMM_GRAM) return;
-    const MUON_GLOBAL uint16_t* E = (KIND == GEMM_POLY) ? gptr(d.A) : gptr(d.X[src]);
-    const int lde = (KIND == GEMM_POLY) ? d.m_pad : d.n_pad;
 #pragma unroll
-    for (int mi = 0; mi < TM; ++mi)
+  for (int mi = 0; mi < TM; ++mi)
 #pragma unroll
-      for (int nj = 0; nj < TN; ++nj)
+    for (int nj = 0; nj < TN; ++nj)
 #pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-          const int i = row0 + wi * (BM / 2) + mi * 32 + (lane & 31);
-          const int j = col0 + wj * (BN / 2) + nj * 32 + 8 * e4 + 4 * (lane >> 5);
-          ein[mi][nj][e4] = *reinterpret_cast<const MUON_GLOBAL u32x2*>(E + (int64_t)i * lde + j);
-        }
+      for (int e4 = 0; e4 < 4; ++e4) ein[mi][nj][e4] = u32x2{0u, 0u};
+  auto capture = [&](int kt) {
+    const LDS_AS char* st = (const LDS_AS char*)lds + (kt % NSTAGE) * STAGE_BYTES;
+    if constexpr (KIND == GEMM_POLY) {
+#pragma unroll
+      for (int nj = 0; nj < TN; ++nj) {
+        const int cbase = col0 + wj * WTN + nj * 32;  // 32 columns inside one K slice
+        if (cbase / BK != kt) continue;
+#pragma unroll
+        for (int mi = 0; mi < TM; ++mi)
+#pragma unroll
+          for (int e4 = 0; e4 < 4; ++e4) {
+            const int ar = wi * WTM + mi * 32 + (lane & 31);
+            const int kl = cbase % BK + 8 * e4 + 4 * (lane >> 5);
+            ein[mi][nj][e4] = *(const LDS_AS u32x2*)(st + ar * 128 + swz_k(ar, kl >> 3) * 16 + (kl & 7) * 2);
+          }
+      }
+    }
   };
 
   // Main loop.  Stage kt is complete once this wave has at most
@@ -256,38 +268,64 @@ __global__ __launch_bounds__(NS_THREADS, 2) void ns_gemm_kernel(const MatDesc* _
   for (int s = 0; s < NSTAGE - 1; ++s)
     if (s < KT) issue(s);
   for (int kt = 0; kt < KT; ++kt) {
-    const int ahead = min(NSTAGE - 2, KT - 1 - kt);
-    if (NSTAGE >= 4 && ahead >= 2)
-      wait_vm_lgkm0<2 * LPW>();
-    else if (ahead >= 1)
+    if (NSTAGE == 3 && kt + 1 < KT)
       wait_vm_lgkm0<LPW>();
     else
       wait_vm_lgkm0<0>();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (kt + NSTAGE - 1 < KT)
-      issue(kt + NSTAGE - 1);
-    else if (kt == KT - 1)
-      eload();
+    if (kt + NSTAGE - 1 < KT) issue(kt + NSTAGE - 1);
+    capture(kt);
     compute(kt);
   }
 
   // Epilogue.  Lane holds, for MFMA tile (mi, nj) and quad e4, output row
-  // i = .. + lane%32 and columns j .. j+3 with j = .. + 8*e4 + 4*(lane/32).
-  // A symmetric tile that reaches below the diagonal stores only i <= j and
-  // mirrors i < j; other symmetric tiles store both triangles' copies.
-  const bool masked = (KIND != GEMM_UPDATE) && (row0 + BM - 1 > col0);
+  // i = wi*WTM + mi*32 + lane%32 and columns j .. j+3 with
+  // j = wj*WTN + nj*32 + 8*e4 + 4*(lane/32) (tile-relative).  Results are
+  // rounded to bf16 and staged in LDS (the pipeline buffers are free now),
+  // then written out as whole 16-byte row segments.
+  wait_vm_lgkm0<0>();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  LDS_AS char* E = (LDS_AS char*)lds;
+  constexpr int ROWB = BN * 2;          // staged row bytes
+  constexpr int RCH = BN / 8;           // 16-byte chunks per staged row
+  static_assert(KIND == GEMM_UPDATE || BM == BN, "symmetric tiles are square");
+  static_assert((KIND == GEMM_UPDATE ? 1 : 2) * BM * ROWB <= NSTAGE * STAGE_BYTES, "staging does not fit");
+  // chunk swizzle of a staged row: spreads a column of 16-byte chunks over the banks
+  auto ech = [&](int r, int c) { return c ^ (r & (RCH - 1) & 31); };
+  const bool diag = (KIND != GEMM_UPDATE) && (row0 == col0);
+  LDS_AS char* E2 = E + BM * ROWB;  // transposed copy (symmetric off-diagonal tiles)
+  if constexpr (KIND == GEMM_UPDATE) {
+    // X[row0 + r][col0 + c] staged in E's own layout (rows past m_pad clamped)
+    constexpr int XI = BM * ROWB / (16 * NT);  // DMA instructions per wave
+    const MUON_GLOBAL uint16_t* Xs = gptr(d.X[src]);
+#pragma unroll
+    for (int q = 0; q < XI; ++q) {
+      const int slot = (wave * XI + q) * 64 + lane;
+      const int r = slot / RCH, pc = slot % RCH;
+      const int gr = min(row0 + r, row_lim - 1);
+      __builtin_amdgcn_global_load_lds((const void*)(d.X[src] + (int64_t)gr * ldc + col0 + ech(r, pc) * 8),
+                                       (LDS_AS void*)(E + (wave * XI + q) * 1024), 16, 0, 0);
+    }
+    (void)Xs;
+    wait_vm_lgkm0<0>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  }
 #pragma unroll
   for (int mi = 0; mi < TM; ++mi) {
 #pragma unroll
     for (int nj = 0; nj < TN; ++nj) {
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
-        const int i = row0 + wi * (BM / 2) + mi * 32 + (lane & 31);
-        const int j = col0 + wj * (BN / 2) + nj * 32 + 8 * e4 + 4 * (lane >> 5);
+        const int r = wi * WTM + mi * 32 + (lane & 31);
+        const int c = wj * WTN + nj * 32 + 8 * e4 + 4 * (lane >> 5);
         float v[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) v[k] = acc[mi][nj][4 * e4 + k];
+        if (KIND == GEMM_UPDATE)
+          ein[mi][nj][e4] = *(const LDS_AS u32x2*)(E + r * ROWB + ech(r, c >> 3) * 16 + (c & 7) * 2);
         if (KIND != GEMM_GRAM) {
           const u32x2 e2 = ein[mi][nj][e4];
           const float ev[4] = {bf16_lo(e2.x), bf16_hi(e2.x), bf16_lo(e2.y), bf16_hi(e2.y)};
@@ -297,24 +335,46 @@ __global__ __launch_bounds__(NS_THREADS, 2) void ns_gemm_kernel(const MatDesc* _
         uint32_t h[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) h[k] = f32_to_bf16_bits(v[k]);
-        if (!masked) {
-          u32x2 o;
-          o.x = h[0] | (h[1] << 16);
-          o.y = h[2] | (h[3] << 16);
-          *reinterpret_cast<MUON_GLOBAL u32x2*>(C + (int64_t)i * ldc + j) = o;
+        if (!diag) {
+          *(LDS_AS u32x2*)(E + r * ROWB + ech(r, c >> 3) * 16 + (c & 7) * 2) =
+              u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
           if (KIND != GEMM_UPDATE) {
 #pragma unroll
-            for (int k = 0; k < 4; ++k) C[(int64_t)(j + k) * ldc + i] = (uint16_t)h[k];
+            for (int k = 0; k < 4; ++k)
+              *(LDS_AS uint16_t*)(E2 + (c + k) * ROWB + ech(c + k, r >> 3) * 16 + (r & 7) * 2) = (uint16_t)h[k];
           }
         } else {
+          // diagonal tile: the upper triangle from this value, the lower by mirroring
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
-            const int jj = j + k;
-            if (i <= jj) C[(int64_t)i * ldc + jj] = (uint16_t)h[k];
-            if (i < jj) C[(int64_t)jj * ldc + i] = (uint16_t)h[k];
+            const int cc2 = c + k;
+            if (r <= cc2) *(LDS_AS uint16_t*)(E + r * ROWB + ech(r, cc2 >> 3) * 16 + (cc2 & 7) * 2) = (uint16_t)h[k];
+            if (r < cc2) *(LDS_AS uint16_t*)(E + cc2 * ROWB + ech(cc2, r >> 3) * 16 + (r & 7) * 2) = (uint16_t)h[k];
           }
         }
       }
+    }
+  }
+  wait_vm_lgkm0<0>();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  constexpr int CHUNKS = BM * RCH;
+  static_assert(CHUNKS % NT == 0, "copy-out split");
+#pragma unroll
+  for (int s = 0; s < CHUNKS / NT; ++s) {
+    const int q = tid + s * NT;
+    const int r = q / RCH, c = q % RCH;
+    const u32x4 val = *(const LDS_AS u32x4*)(E + r * ROWB + ech(r, c) * 16);
+    if (row0 + r < row_lim)
+      *reinterpret_cast<MUON_GLOBAL u32x4*>(C + (int64_t)(row0 + r) * ldc + col0 + c * 8) = val;
+  }
+  if (KIND != GEMM_UPDATE && !diag) {
+#pragma unroll
+    for (int s = 0; s < CHUNKS / NT; ++s) {
+      const int q = tid + s * NT;
+      const int r = q / RCH, c = q % RCH;
+      const u32x4 val = *(const LDS_AS u32x4*)(E2 + r * ROWB + ech(r, c) * 16);
+      *reinterpret_cast<MUON_GLOBAL u32x4*>(C + (int64_t)(col0 + r) * ldc + row0 + c * 8) = val;
     }
   }
 }
@@ -324,13 +384,13 @@ hipError_t launch_gemm(int kind, const MatDesc* d, const GemmItem* items, int n_
   if (n_items == 0) return hipSuccess;
   switch (kind) {
     case GEMM_GRAM:
-      ns_gemm_kernel<GEMM_GRAM, SYM_BM, SYM_BN, 4><<<n_items, NS_THREADS, 0, s>>>(d, items, src, ca, cb, cc);
+      ns_gemm_kernel<GEMM_GRAM, SYM_BM, SYM_BN, 2, 2, 2><<<n_items, 256, 0, s>>>(d, items, src, ca, cb, cc);
       break;
     case GEMM_POLY:
-      ns_gemm_kernel<GEMM_POLY, SYM_BM, SYM_BN, 4><<<n_items, NS_THREADS, 0, s>>>(d, items, src, ca, cb, cc);
+      ns_gemm_kernel<GEMM_POLY, SYM_BM, SYM_BN, 2, 2, 2><<<n_items, 256, 0, s>>>(d, items, src, ca, cb, cc);
       break;
     default:
-      ns_gemm_kernel<GEMM_UPDATE, UPD_BM, UPD_BN, 3><<<n_items, NS_THREADS, 0, s>>>(d, items, src, ca, cb, cc);
+      ns_gemm_kernel<GEMM_UPDATE, UPD_BM, UPD_BN, 2, 4, 2><<<n_items, 512, 0, s>>>(d, items, src, ca, cb, cc);
       break;
   }
   return hipGetLastError();

@@ -311,7 +311,7 @@ int get_plan(DeviceState& st, int mode, int n, const muon_shape_t* shapes, float
         gram_cost.push_back(desc[i].n_pad);
       }
     for (int tj = 0; tj < tn; ++tj)
-      for (int ti = 0; ti < desc[i].m_pad / UPD_BM; ++ti) {
+      for (int ti = 0; ti < desc[i].m_pad / 128; ti += UPD_BM / 128) {
         upd_seq.push_back({i, (int16_t)ti, (int16_t)tj});
         upd_cost.push_back(desc[i].m_pad);
       }
