@@ -27,9 +27,11 @@ __device__ __forceinline__ const MUON_GLOBAL T* gptr(const T* p) {
 }
 
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t quiet_nan = (u >> 16) | 0x40u;
+  // select, not branch: this runs once per element of every epilogue
+  return ((u & 0x7fffffffu) > 0x7f800000u) ? quiet_nan : rounded;
 }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {

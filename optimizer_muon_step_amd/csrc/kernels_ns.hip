@@ -58,7 +58,10 @@ __device__ __forceinline__ int swz_k(int row, int chunk) { return chunk ^ ((row 
 // k-major tile: rows of BN*2 bytes.  A transposing read has each 16-lane
 // group on 4 consecutive rows, 32 bytes each, and pairs of groups 32 bytes
 // apart; XOR by 4(r%4) moves the 4 rows into different 64-byte bank groups.
-__device__ __forceinline__ int swz_n(int row, int chunk) { return chunk ^ (4 * (row & 3)); }
+// The extra XOR by (r/4)%4 stays inside each 64-byte group (so the
+// transposing reads keep their banks) and spreads the epilogue's reads of
+// one column over 32 consecutive rows across 16 chunks.
+__device__ __forceinline__ int swz_n(int row, int chunk) { return chunk ^ (4 * (row & 3)) ^ ((row >> 2) & 3); }
 
 // B fragments of one k-step from a k-major LDS tile: two transposing reads
 // per 32-column fragment (ds_read_b64_tr_b16 transposes 16-bit elements
@@ -84,9 +87,30 @@ __device__ __forceinline__ void read_tr_frags2(bf16x8* bfr, uint32_t a0, uint32_
   bfr[1] = __builtin_bit_cast(bf16x8, u32x4{(uint32_t)r2, (uint32_t)(r2 >> 32), (uint32_t)r3, (uint32_t)(r3 >> 32)});
 }
 
+__device__ __forceinline__ void read_tr_frags4(bf16x8* bfr, const uint32_t* a) {
+  uint64_t r[8];
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %9\n\t"
+      "ds_read_b64_tr_b16 %2, %10\n\t"
+      "ds_read_b64_tr_b16 %3, %11\n\t"
+      "ds_read_b64_tr_b16 %4, %12\n\t"
+      "ds_read_b64_tr_b16 %5, %13\n\t"
+      "ds_read_b64_tr_b16 %6, %14\n\t"
+      "ds_read_b64_tr_b16 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+      : "memory");
+#pragma unroll
+  for (int nj = 0; nj < 4; ++nj)
+    bfr[nj] = __builtin_bit_cast(bf16x8, u32x4{(uint32_t)r[2 * nj], (uint32_t)(r[2 * nj] >> 32),
+                                               (uint32_t)r[2 * nj + 1], (uint32_t)(r[2 * nj + 1] >> 32)});
+}
+
 }  // namespace
 
-template <int KIND, int BM, int BN, int WAVES_M, int WAVES_N, int NSTAGE>
+template <int KIND, int BM, int BN, int WAVES_M, int WAVES_N, int NSTAGE, int ROWU>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const MatDesc* __restrict__ descs,
                                                                         const GemmItem* __restrict__ items,
                                                                         int src, float ca, float cb, float cc) {
@@ -100,12 +124,18 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const M
   constexpr int B_INSTR = B_BYTES / (16 * NT);
   constexpr int LPW = A_INSTR + B_INSTR;
   constexpr int NCHUNK_N = BN / 8;  // chunks per k-major row
+  // UPDATE: K slices holding the tile's own rows, and the ones kept past the
+  // two stage buffers so that all of them are in LDS when the loop ends.
+  constexpr int OWN = NN ? BM / BK : 0;
+  constexpr int EXTRA = (OWN > 2) ? OWN - 2 : 0;
   static_assert(A_INSTR >= 1 && B_INSTR >= 1 && A_INSTR * 16 * NT == A_BYTES && B_INSTR * 16 * NT == B_BYTES,
                 "tile does not split into whole DMA instructions");
   static_assert(NSTAGE >= 2 && NSTAGE <= 3 && TM >= 1 && TN >= 1, "unsupported tile");
-  static_assert(!NN || TN == 2, "the transposing read path is written for two fragments per wave");
+  static_assert(!NN || ((TN == 2 || TN == 4) && NSTAGE == 2 && BM % BK == 0 && OWN <= 3 && ROWU == BK),
+                "UPDATE tiling: 2 stages, tile rows a whole number (<= 3) of K slices");
+  static_assert(NN || ROWU == BM, "symmetric tiles are addressed in units of their own size");
   static_assert(!NN || BN >= 128, "k-major swizzle needs 16 chunks per row");
-  __shared__ __attribute__((aligned(16))) char lds[NSTAGE * STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) char lds[NSTAGE * STAGE_BYTES + EXTRA * B_BYTES];
 
   const GemmItem it = items[blockIdx.x];
   if (it.mat < 0) return;  // padding item of a shorter per-XCD run
@@ -122,49 +152,72 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const M
     Aop = d.B; lda = d.m_pad; Bop = d.X[src]; ldb = d.n_pad; K = d.m_pad; C = gptr(d.X[src ^ 1]);
     ldc = d.n_pad;
   }
-  // Output rows are rows of Aop; tile rows are counted in units of 128 so a
-  // BM = 256 tile may hang over the last 128-row block of m_pad.  Such rows
-  // load a clamped (valid) row, compute values that are never stored.
-  const int row0 = it.ti * 128;
+  // Output rows are rows of Aop.  An UPDATE tile starts at a multiple of
+  // ROWU = 64 rows and may hang over m_pad: its rows past m_pad fetch rows of
+  // the A/B buffers' spare block, compute values that are never stored.
+  const int row0 = it.ti * ROWU;
   const int col0 = it.tj * BN;  // output columns: rows of Bop (GRAM/POLY), columns of X (UPDATE)
   const int row_lim = d.m_pad;
+  const int KT = K / BK;
+
+  // K order.  UPDATE visits the slices holding its own rows last, so that
+  // when the loop ends they are still in LDS (the last two stage buffers,
+  // plus one slice copied aside) for the a*X term of the epilogue.  The order
+  // of the fp32 sum is the only thing that changes.
+  int n_own = 0, kt0 = 0;
+  if (NN) {
+    n_own = min(OWN, KT - row0 / BK);
+    kt0 = (row0 / BK + n_own) % KT;
+  }
+  auto kt_of = [&](int s) { int k = kt0 + s; return k >= KT ? k - KT : k; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wi = wave / WAVES_N, wj = wave % WAVES_N;
 
-  // Per-lane global source of each DMA instruction at k = 0 (element offsets).
-  int64_t a_off[A_INSTR], b_off[B_INSTR];
+  // DMA sources.  Instruction q of this wave fills LDS slots
+  // g*64 + lane, g = wave*INSTR + q; its rows are a wave-uniform base plus a
+  // lane part, and the swizzle depends on g only through g % 2, so each
+  // operand needs two per-lane offsets.
+  int a_vo[2], b_vo[2];
 #pragma unroll
-  for (int q = 0; q < A_INSTR; ++q) {
-    const int s = (wave * A_INSTR + q) * 64 + lane;
-    const int row = s >> 3;
-    a_off[q] = (int64_t)min(row0 + row, row_lim - 1) * lda + swz_k(row, s & 7) * 8;
-  }
-#pragma unroll
-  for (int q = 0; q < B_INSTR; ++q) {
-    const int s = (wave * B_INSTR + q) * 64 + lane;
+  for (int p = 0; p < 2; ++p) {
+    {
+      const int row = p * 8 + (lane >> 3);  // row within a pair of instructions
+      a_vo[p] = (lane >> 3) * lda + swz_k(row, lane & 7) * 8;
+    }
     if (!NN) {
-      const int row = s >> 3;
-      b_off[q] = (int64_t)(col0 + row) * ldb + swz_k(row, s & 7) * 8;
+      const int row = p * 8 + (lane >> 3);
+      b_vo[p] = (lane >> 3) * ldb + swz_k(row, lane & 7) * 8;
     } else {
-      const int row = s / NCHUNK_N;
-      b_off[q] = (int64_t)row * ldb + col0 + swz_n(row, s % NCHUNK_N) * 8;
+      b_vo[p] = 0;  // k-major: the swizzle depends on more than g % 2, computed per instruction
     }
   }
-  auto issue = [&](int kt) {
-    LDS_AS char* st = (LDS_AS char*)lds + (kt % NSTAGE) * STAGE_BYTES;
-    const int64_t ka = (int64_t)kt * BK;
-    const int64_t kb = NN ? (int64_t)kt * BK * ldb : (int64_t)kt * BK;
+  auto issue = [&](int s) {
+    const int kt = kt_of(s);
+    LDS_AS char* st = (LDS_AS char*)lds + (s % NSTAGE) * STAGE_BYTES;
 #pragma unroll
-    for (int q = 0; q < A_INSTR; ++q)
-      __builtin_amdgcn_global_load_lds((const void*)(Aop + a_off[q] + ka),
-                                       (LDS_AS void*)(st + (wave * A_INSTR + q) * 1024), 16, 0, 0);
+    for (int q = 0; q < A_INSTR; ++q) {
+      const int g = wave * A_INSTR + q;
+      const uint16_t* src_row = Aop + (int64_t)(row0 + g * 8) * lda + (int64_t)kt * BK;
+      __builtin_amdgcn_global_load_lds((const void*)(src_row + a_vo[g & 1]), (LDS_AS void*)(st + g * 1024), 16, 0, 0);
+    }
 #pragma unroll
-    for (int q = 0; q < B_INSTR; ++q)
-      __builtin_amdgcn_global_load_lds((const void*)(Bop + b_off[q] + kb),
-                                       (LDS_AS void*)(st + A_BYTES + (wave * B_INSTR + q) * 1024), 16, 0, 0);
+    for (int q = 0; q < B_INSTR; ++q) {
+      const int g = wave * B_INSTR + q;
+      const uint16_t* src_row;
+      int vo;
+      if (NN) {
+        const int row = g * (64 / NCHUNK_N) + lane / NCHUNK_N;  // row within the slice
+        src_row = Bop + (int64_t)(kt * BK + g * (64 / NCHUNK_N)) * ldb + col0;
+        vo = (lane / NCHUNK_N) * ldb + swz_n(row, lane % NCHUNK_N) * 8;
+      } else {
+        src_row = Bop + (int64_t)(col0 + g * 8) * ldb + (int64_t)kt * BK;
+        vo = b_vo[g & 1];
+      }
+      __builtin_amdgcn_global_load_lds((const void*)(src_row + vo), (LDS_AS void*)(st + A_BYTES + g * 1024), 16, 0, 0);
+    }
   };
 
   floatx16 acc[TM][TN];
@@ -200,39 +253,80 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const M
     }
   }
 
-  auto compute = [&](int kt) {
-    const LDS_AS char* st = (const LDS_AS char*)lds + (kt % NSTAGE) * STAGE_BYTES;
+  auto read_a_rows = [&](const LDS_AS char* st, int kk, int m0, int m1, bf16x8* af) {
+    // k-step kk reads logical chunk 2kk + lane/32; the swizzle is an XOR, so
+    // that is the k-step-0 chunk XOR 2kk, i.e. the byte offset XOR 32kk.
+#pragma unroll
+    for (int mi = m0; mi < m1; ++mi)
+      af[mi] = __builtin_bit_cast(bf16x8, *(const LDS_AS u32x4*)(st + (a_rd[mi] ^ (32 * kk))));
+  };
+  auto read_b_tr = [&](uint32_t st_addr, int kk, bf16x8* bfr) {
+    // k-step kk is 16 rows further on; (row % 4), hence the swizzle, is unchanged
+    const uint32_t dk = st_addr + kk * 16 * (BN * 2);
+    if constexpr (TN == 2) {
+      read_tr_frags2(bfr, dk + b_rd[0][0], dk + b_rd[0][1], dk + b_rd[1][0], dk + b_rd[1][1]);
+    } else {
+      uint32_t ad[8];
+#pragma unroll
+      for (int nj = 0; nj < 4; ++nj) {
+        ad[2 * nj] = dk + b_rd[nj][0];
+        ad[2 * nj + 1] = dk + b_rd[nj][1];
+      }
+      read_tr_frags4(bfr, ad);
+    }
+  };
+  auto mfma_rows = [&](int m0, int m1, const bf16x8* af, const bf16x8* bfr) {
+    // operands swapped so each lane ends up with 4 consecutive output columns
+#pragma unroll
+    for (int mi = m0; mi < m1; ++mi)
+#pragma unroll
+      for (int nj = 0; nj < TN; ++nj)
+        acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[nj], af[mi], acc[mi][nj], 0, 0, 0);
+  };
+
+  auto compute = [&](int s) {
+    const LDS_AS char* st = (const LDS_AS char*)lds + (s % NSTAGE) * STAGE_BYTES;
     const uint32_t st_addr = (uint32_t)(uintptr_t)st;
+    if constexpr (!NN) {
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8 af[TM], bfr[TN];
-      // k-step kk reads logical chunk 2kk + lane/32; the swizzle is an XOR, so
-      // that is the k-step-0 chunk XOR 2kk, i.e. the byte offset XOR 32kk.
-#pragma unroll
-      for (int mi = 0; mi < TM; ++mi)
-        af[mi] = __builtin_bit_cast(bf16x8, *(const LDS_AS u32x4*)(st + (a_rd[mi] ^ (32 * kk))));
-      if constexpr (!NN) {
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        bf16x8 af[TM], bfr[TN];
+        read_a_rows(st, kk, 0, TM, af);
 #pragma unroll
         for (int nj = 0; nj < TN; ++nj)
           bfr[nj] = __builtin_bit_cast(bf16x8, *(const LDS_AS u32x4*)(st + (b_rd[nj][0] ^ (32 * kk))));
-      } else {
-        // k-step kk is 16 rows further on; (row % 4), hence the swizzle, is unchanged
-        const uint32_t dk = st_addr + kk * 16 * (BN * 2);
-        read_tr_frags2(bfr, dk + b_rd[0][0], dk + b_rd[0][1], dk + b_rd[1][0], dk + b_rd[1][1]);
+        mfma_rows(0, TM, af, bfr);
       }
-      // operands swapped so each lane ends up with 4 consecutive output columns
+    } else {
+      // Operands of k-step kk+1 are read between the two halves of k-step kk's
+      // MFMAs, so the read block's closing wait overlaps queued MFMA work.  A
+      // fragments: the first half is refreshed for kk+1 once its MFMAs have
+      // issued; the second half is read for kk at the start of the step.
+      constexpr int MH = (TM + 1) / 2;
+      bf16x8 af[TM], bfr[2][TN];
+      read_a_rows(st, 0, 0, MH, af);
+      read_b_tr(st_addr, 0, bfr[0]);
 #pragma unroll
-      for (int mi = 0; mi < TM; ++mi)
-#pragma unroll
-        for (int nj = 0; nj < TN; ++nj)
-          acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[nj], af[mi], acc[mi][nj], 0, 0, 0);
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        const int cur = kk & 1;
+        read_a_rows(st, kk, MH, TM, af);
+        mfma_rows(0, MH, af, bfr[cur]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (kk + 1 < BK / 16) {
+          read_a_rows(st, kk + 1, 0, MH, af);
+          read_b_tr(st_addr, kk + 1, bfr[cur ^ 1]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_rows(MH, TM, af, bfr[cur]);
+      }
     }
   };
 
-  // POLY's b*A term needs A[i][j], which is column k = j of the staged A tile:
-  // it is read out of the K slice that holds it (no extra global traffic).
-  // UPDATE's a*X term is fetched into LDS after the main loop instead
-  // (holding it in registers through the loop would exceed the budget).
+  // Epilogue inputs come out of staged K slices that already hold them, so
+  // they cost no extra global traffic.  POLY: A[i][j] is column k = j of the
+  // A slice, picked up during the loop.  UPDATE: X[i][j] is row k = i of the
+  // k-major X slice, read after the loop from the slices kept in LDS.  The
+  // epilogue combines them in the fixed order of the storage-point reading.
   u32x2 ein[TM][TN][4];
 #pragma unroll
   for (int mi = 0; mi < TM; ++mi)
@@ -240,43 +334,55 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const M
     for (int nj = 0; nj < TN; ++nj)
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) ein[mi][nj][e4] = u32x2{0u, 0u};
-  auto capture = [&](int kt) {
-    const LDS_AS char* st = (const LDS_AS char*)lds + (kt % NSTAGE) * STAGE_BYTES;
-    if constexpr (KIND == GEMM_POLY) {
+  auto capture_poly = [&](int s) {
+    const LDS_AS char* st = (const LDS_AS char*)lds + (s % NSTAGE) * STAGE_BYTES;
+    const int kt = kt_of(s);
 #pragma unroll
-      for (int nj = 0; nj < TN; ++nj) {
-        const int cbase = col0 + wj * WTN + nj * 32;  // 32 columns inside one K slice
-        if (cbase / BK != kt) continue;
+    for (int nj = 0; nj < TN; ++nj) {
+      const int cbase = col0 + wj * WTN + nj * 32;  // 32 columns inside one K slice
+      if (cbase / BK != kt) continue;
 #pragma unroll
-        for (int mi = 0; mi < TM; ++mi)
+      for (int mi = 0; mi < TM; ++mi)
 #pragma unroll
-          for (int e4 = 0; e4 < 4; ++e4) {
-            const int ar = wi * WTM + mi * 32 + (lane & 31);
-            const int kl = cbase % BK + 8 * e4 + 4 * (lane >> 5);
-            ein[mi][nj][e4] = *(const LDS_AS u32x2*)(st + ar * 128 + swz_k(ar, kl >> 3) * 16 + (kl & 7) * 2);
-          }
-      }
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const int ar = wi * WTM + mi * 32 + (lane & 31);
+          const int kl = cbase % BK + 8 * e4 + 4 * (lane >> 5);
+          ein[mi][nj][e4] = *(const LDS_AS u32x2*)(st + ar * 128 + swz_k(ar, kl >> 3) * 16 + (kl & 7) * 2);
+        }
     }
   };
+  LDS_AS char* const extra = (LDS_AS char*)lds + NSTAGE * STAGE_BYTES;
+  // UPDATE: an own slice that is not among the last two is copied aside
+  // (16-byte chunks, all threads) before its stage buffer is refilled.
+  auto keep_slice = [&](int s) {
+    const int slot = s - (KT - n_own);
+    if (slot < 0 || slot >= n_own - 2) return;
+    const LDS_AS char* from = (const LDS_AS char*)lds + (s % NSTAGE) * STAGE_BYTES + A_BYTES;
+    LDS_AS char* to = extra + slot * B_BYTES;
+#pragma unroll
+    for (int c = 0; c < B_BYTES / (16 * NT); ++c)
+      *(LDS_AS u32x4*)(to + (c * NT + tid) * 16) = *(const LDS_AS u32x4*)(from + (c * NT + tid) * 16);
+  };
 
-  // Main loop.  Stage kt is complete once this wave has at most
-  // (stages issued after kt) x LPW DMA operations outstanding and every wave
-  // has passed the barrier; the buffer refilled next was last read in kt-1,
-  // which every wave finished (its LDS reads included) before the barrier.
-  const int KT = K / BK;
+  // Main loop over s = 0 .. KT-1 (slice kt_of(s), stage buffer s % NSTAGE).
+  // Slice s is complete once this wave has at most (slices issued after it)
+  // x LPW DMA operations outstanding and every wave has passed the barrier;
+  // the buffer refilled next was last read in step s-1, which every wave
+  // finished (its LDS reads included) before the barrier.
 #pragma unroll
   for (int s = 0; s < NSTAGE - 1; ++s)
     if (s < KT) issue(s);
-  for (int kt = 0; kt < KT; ++kt) {
-    if (NSTAGE == 3 && kt + 1 < KT)
+  for (int s = 0; s < KT; ++s) {
+    if (NSTAGE == 3 && s + 1 < KT)
       wait_vm_lgkm0<LPW>();
     else
       wait_vm_lgkm0<0>();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (kt + NSTAGE - 1 < KT) issue(kt + NSTAGE - 1);
-    capture(kt);
-    compute(kt);
+    if (s + NSTAGE - 1 < KT) issue(s + NSTAGE - 1);
+    if constexpr (KIND == GEMM_POLY) capture_poly(s);
+    if constexpr (EXTRA > 0) keep_slice(s);
+    compute(s);
   }
 
   // Epilogue.  Lane holds, for MFMA tile (mi, nj) and quad e4, output row
@@ -287,6 +393,29 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const M
   wait_vm_lgkm0<0>();
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+  if constexpr (NN) {
+    // own slice j (rows j*BK .. of the tile) was step KT - n_own + j
+#pragma unroll
+    for (int mi = 0; mi < TM; ++mi) {
+      const int tr = wi * WTM + mi * 32;  // tile row of this 32-row block
+      const int j = tr / BK;
+      if (j >= n_own) continue;  // rows past m_pad: never stored
+      const int step = KT - n_own + j;
+      const LDS_AS char* slice = (step >= KT - 2) ? (const LDS_AS char*)lds + (step % NSTAGE) * STAGE_BYTES + A_BYTES
+                                                  : (const LDS_AS char*)extra + j * B_BYTES;
+      const int lr = tr % BK + (lane & 31);
+#pragma unroll
+      for (int nj = 0; nj < TN; ++nj)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const int cl = wj * WTN + nj * 32 + 8 * e4 + 4 * (lane >> 5);
+          ein[mi][nj][e4] = *(const LDS_AS u32x2*)(slice + lr * (BN * 2) + swz_n(lr, cl >> 3) * 16 + (cl & 7) * 2);
+        }
+    }
+    wait_vm_lgkm0<0>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  }
   LDS_AS char* E = (LDS_AS char*)lds;
   constexpr int ROWB = BN * 2;          // staged row bytes
   constexpr int RCH = BN / 8;           // 16-byte chunks per staged row
@@ -296,23 +425,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const M
   auto ech = [&](int r, int c) { return c ^ (r & (RCH - 1) & 31); };
   const bool diag = (KIND != GEMM_UPDATE) && (row0 == col0);
   LDS_AS char* E2 = E + BM * ROWB;  // transposed copy (symmetric off-diagonal tiles)
-  if constexpr (KIND == GEMM_UPDATE) {
-    // X[row0 + r][col0 + c] staged in E's own layout (rows past m_pad clamped)
-    constexpr int XI = BM * ROWB / (16 * NT);  // DMA instructions per wave
-    const MUON_GLOBAL uint16_t* Xs = gptr(d.X[src]);
-#pragma unroll
-    for (int q = 0; q < XI; ++q) {
-      const int slot = (wave * XI + q) * 64 + lane;
-      const int r = slot / RCH, pc = slot % RCH;
-      const int gr = min(row0 + r, row_lim - 1);
-      __builtin_amdgcn_global_load_lds((const void*)(d.X[src] + (int64_t)gr * ldc + col0 + ech(r, pc) * 8),
-                                       (LDS_AS void*)(E + (wave * XI + q) * 1024), 16, 0, 0);
-    }
-    (void)Xs;
-    wait_vm_lgkm0<0>();
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-  }
 #pragma unroll
   for (int mi = 0; mi < TM; ++mi) {
 #pragma unroll
@@ -324,8 +436,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const M
         float v[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) v[k] = acc[mi][nj][4 * e4 + k];
-        if (KIND == GEMM_UPDATE)
-          ein[mi][nj][e4] = *(const LDS_AS u32x2*)(E + r * ROWB + ech(r, c >> 3) * 16 + (c & 7) * 2);
         if (KIND != GEMM_GRAM) {
           const u32x2 e2 = ein[mi][nj][e4];
           const float ev[4] = {bf16_lo(e2.x), bf16_hi(e2.x), bf16_lo(e2.y), bf16_hi(e2.y)};
@@ -384,13 +494,13 @@ hipError_t launch_gemm(int kind, const MatDesc* d, const GemmItem* items, int n_
   if (n_items == 0) return hipSuccess;
   switch (kind) {
     case GEMM_GRAM:
-      ns_gemm_kernel<GEMM_GRAM, SYM_BM, SYM_BN, 2, 2, 2><<<n_items, 256, 0, s>>>(d, items, src, ca, cb, cc);
+      ns_gemm_kernel<GEMM_GRAM, SYM_BM, SYM_BN, 2, 2, 2, SYM_BM><<<n_items, 256, 0, s>>>(d, items, src, ca, cb, cc);
       break;
     case GEMM_POLY:
-      ns_gemm_kernel<GEMM_POLY, SYM_BM, SYM_BN, 2, 2, 2><<<n_items, 256, 0, s>>>(d, items, src, ca, cb, cc);
+      ns_gemm_kernel<GEMM_POLY, SYM_BM, SYM_BN, 2, 2, 2, SYM_BM><<<n_items, 256, 0, s>>>(d, items, src, ca, cb, cc);
       break;
     default:
-      ns_gemm_kernel<GEMM_UPDATE, UPD_BM, UPD_BN, 2, 4, 2><<<n_items, 512, 0, s>>>(d, items, src, ca, cb, cc);
+      ns_gemm_kernel<GEMM_UPDATE, UPD_BM, UPD_BN, 2, 4, 2, UPD_ROWU><<<n_items, 512, 0, s>>>(d, items, src, ca, cb, cc);
       break;
   }
   return hipGetLastError();

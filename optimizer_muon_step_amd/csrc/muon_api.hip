@@ -65,7 +65,10 @@ Geometry geometry_of(const muon_shape_t& s) {
   g.n_pad = (int32_t)round_up(g.n, NS_PAD_N);
   g.part_cnt = (int32_t)((s.rows * s.cols + MOM_CHUNK - 1) / MOM_CHUNK);
   g.x_bytes = align_up((size_t)g.m_pad * g.n_pad * 2);
-  g.a_bytes = align_up((size_t)g.m_pad * g.m_pad * 2);
+  // A and B carry NS_PAD_M spare rows: an update tile may hang over the last
+  // rows and fetch (never store) up to UPD_BM - UPD_ROWU rows past m_pad.
+  static_assert(UPD_BM - UPD_ROWU <= NS_PAD_M, "spare rows");
+  g.a_bytes = align_up((size_t)(g.m_pad + NS_PAD_M) * g.m_pad * 2);
   g.part_bytes = align_up((size_t)g.part_cnt * sizeof(double));
   return g;
 }
@@ -311,7 +314,7 @@ int get_plan(DeviceState& st, int mode, int n, const muon_shape_t* shapes, float
         gram_cost.push_back(desc[i].n_pad);
       }
     for (int tj = 0; tj < tn; ++tj)
-      for (int ti = 0; ti < desc[i].m_pad / 128; ti += UPD_BM / 128) {
+      for (int ti = 0; ti < desc[i].m_pad / UPD_ROWU; ti += UPD_BM / UPD_ROWU) {
         upd_seq.push_back({i, (int16_t)ti, (int16_t)tj});
         upd_cost.push_back(desc[i].m_pad);
       }
