@@ -94,7 +94,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--kernel-breakdown", action="store_true", help="also time every kernel family")
+    ap.add_argument("--no-kernel-breakdown", action="store_true",
+                    help="skip the per-kernel-family timing pass after the timed region")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -130,20 +131,21 @@ def main():
     # Timed region: K steps; the update GEMM's launches are bracketed by HIP
     # events on this stream.
     mu.muon_timing_enable(mu.KERNEL_UPDATE)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
+    evs[0].record(stream)
+    for k in range(args.steps):
         step()
-    ev1.record(stream)
+        evs[k + 1].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     upd_ms_total, upd_launches = mu.muon_timing_read()
     mu.muon_timing_enable(-1)
     wall_s = t1 - t0
     ms_per_step = wall_s * 1e3 / args.steps
-    ev_ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    ev_ms_per_step = evs[0].elapsed_time(evs[-1]) / args.steps
+    step_ms = np.array([evs[k].elapsed_time(evs[k + 1]) for k in range(args.steps)])
 
     gram_f, poly_f, upd_f = ns_flops(shapes)
     ns_flops_step = NS_STEPS * (gram_f + poly_f + upd_f)
@@ -151,7 +153,7 @@ def main():
     upd_tflops = upd_f / (upd_ms * 1e-3) / 1e12
 
     breakdown = None
-    if args.kernel_breakdown:
+    if not args.no_kernel_breakdown:
         names = ["momentum", "cast", "gram", "poly", "update", "apply"]
         per_launch_work = [12 * n_params, 10 * n_params, gram_f, poly_f, upd_f, 10 * n_params]
         breakdown = {}
@@ -171,6 +173,10 @@ def main():
                 breakdown[name] = {"ms_per_launch": round(per, 5), "launches_per_step": cnt // 20,
                                    "GB/s": round(ach, 1), "frac_hbm_peak": round(ach / PEAK_HBM_GBS, 4)}
         torch.cuda.synchronize()
+        ns_ms = sum(breakdown[k]["ms_per_launch"] * breakdown[k]["launches_per_step"] for k in ("gram", "poly", "update"))
+        ns_tf = ns_flops_step / (ns_ms * 1e-3) / 1e12
+        breakdown["ns_all"] = {"ms_per_step": round(ns_ms, 5), "TFLOP/s": round(ns_tf, 1),
+                               "frac_bf16_peak": round(ns_tf / PEAK_BF16_TFLOPS, 4)}
 
     # A plain copy of known size, outside the timed region: it calibrates
     # rocprofv3's FETCH_SIZE / WRITE_SIZE counters when this script is profiled.
@@ -190,6 +196,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "ms_per_step_hip_events": round(ev_ms_per_step, 5),
+        "step_ms_p10_p50_p90": [round(float(np.percentile(step_ms, q)), 5) for q in (10, 50, 90)],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
