@@ -191,7 +191,7 @@ __global__ __launch_bounds__(EW_THREADS) void cast_kernel(const MatDesc* __restr
       u32x2 w;
       w.x = pack_bf16x2(v[q][0], v[q][1]);
       w.y = pack_bf16x2(v[q][2], v[q][3]);
-      *reinterpret_cast<MUON_GLOBAL u32x2*>(X + (int64_t)(i0 + tr + 16 * q) * d.n_pad + j0 + tc) = w;
+      *reinterpret_cast<MUON_GLOBAL u32x2*>(X + (int64_t)(i0 + tr + 16 * q) * d.ld_x + j0 + tc) = w;
     }
   } else {
     // canonical (i, j) comes from source (j, i): stage a source tile whose
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(EW_THREADS) void cast_kernel(const MatDesc* __restr
       u32x2 w;
       w.x = pack_bf16x2(T[tc + 0][il], T[tc + 1][il]);
       w.y = pack_bf16x2(T[tc + 2][il], T[tc + 3][il]);
-      *reinterpret_cast<MUON_GLOBAL u32x2*>(X + (int64_t)(i0 + il) * d.n_pad + j0 + tc) = w;
+      *reinterpret_cast<MUON_GLOBAL u32x2*>(X + (int64_t)(i0 + il) * d.ld_x + j0 + tc) = w;
     }
   }
 }
@@ -232,7 +232,7 @@ __global__ __launch_bounds__(EW_THREADS) void apply_kernel(const MatDesc* __rest
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int r = min(r0 + tr + 16 * q, d.m_pad - 1);
-      const u32x2 w = *reinterpret_cast<const MUON_GLOBAL u32x2*>(X + (int64_t)r * d.n_pad + c0 + tc);
+      const u32x2 w = *reinterpret_cast<const MUON_GLOBAL u32x2*>(X + (int64_t)r * d.ld_x + c0 + tc);
       h[q][0] = w.x & 0xffffu;
       h[q][1] = w.x >> 16;
       h[q][2] = w.y & 0xffffu;
@@ -243,7 +243,7 @@ __global__ __launch_bounds__(EW_THREADS) void apply_kernel(const MatDesc* __rest
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int xr = c0 + tr + 16 * q;
-      const u32x2 w = *reinterpret_cast<const MUON_GLOBAL u32x2*>(X + (int64_t)xr * d.n_pad + r0 + tc);
+      const u32x2 w = *reinterpret_cast<const MUON_GLOBAL u32x2*>(X + (int64_t)xr * d.ld_x + r0 + tc);
       T[tr + 16 * q][tc + 0] = (uint16_t)(w.x & 0xffffu);
       T[tr + 16 * q][tc + 1] = (uint16_t)(w.x >> 16);
       T[tr + 16 * q][tc + 2] = (uint16_t)(w.y & 0xffffu);

@@ -131,8 +131,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const M
   static_assert(A_INSTR >= 1 && B_INSTR >= 1 && A_INSTR * 16 * NT == A_BYTES && B_INSTR * 16 * NT == B_BYTES,
                 "tile does not split into whole DMA instructions");
   static_assert(NSTAGE >= 2 && NSTAGE <= 3 && TM >= 1 && TN >= 1, "unsupported tile");
-  static_assert(!NN || ((TN == 2 || TN == 4) && NSTAGE == 2 && BM % BK == 0 && OWN <= 3 && ROWU == BK),
-                "UPDATE tiling: 2 stages, tile rows a whole number (<= 3) of K slices");
+  static_assert(!NN || ((TN == 2 || TN == 4) && BM % BK == 0 && OWN <= 3 && ROWU == BK && (NSTAGE == 2 || OWN <= 2)),
+                "UPDATE tiling: tile rows a whole number (<= 3) of K slices, kept in the ring or aside");
   static_assert(NN || ROWU == BM, "symmetric tiles are addressed in units of their own size");
   static_assert(!NN || BN >= 128, "k-major swizzle needs 16 chunks per row");
   __shared__ __attribute__((aligned(16))) char lds[NSTAGE * STAGE_BYTES + EXTRA * B_BYTES];
@@ -145,12 +145,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const M
   MUON_GLOBAL uint16_t* C;
   int lda, ldb, ldc, K;
   if (KIND == GEMM_GRAM) {
-    Aop = d.X[src]; Bop = Aop; lda = ldb = d.n_pad; K = d.n_pad; C = gptr(d.A); ldc = d.m_pad;
+    Aop = d.X[src]; Bop = Aop; lda = ldb = d.ld_x; K = d.n_pad; C = gptr(d.A); ldc = d.ld_a;
   } else if (KIND == GEMM_POLY) {
-    Aop = d.A; Bop = Aop; lda = ldb = d.m_pad; K = d.m_pad; C = gptr(d.B); ldc = d.m_pad;
+    Aop = d.A; Bop = Aop; lda = ldb = d.ld_a; K = d.m_pad; C = gptr(d.B); ldc = d.ld_a;
   } else {
-    Aop = d.B; lda = d.m_pad; Bop = d.X[src]; ldb = d.n_pad; K = d.m_pad; C = gptr(d.X[src ^ 1]);
-    ldc = d.n_pad;
+    Aop = d.B; lda = d.ld_a; Bop = d.X[src]; ldb = d.ld_x; K = d.m_pad; C = gptr(d.X[src ^ 1]);
+    ldc = d.ld_x;
   }
   // Output rows are rows of Aop.  An UPDATE tile starts at a multiple of
   // ROWU = 64 rows and may hang over m_pad: its rows past m_pad fetch rows of

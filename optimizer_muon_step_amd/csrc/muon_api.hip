@@ -50,7 +50,7 @@ constexpr size_t kScaleBytes = sizeof(float) * MUON_MAX_MATRICES;
 constexpr size_t kControlBytes = kScaleBytes;
 
 struct Geometry {
-  int32_t rows, cols, m, n, m_pad, n_pad, transposed, part_cnt;
+  int32_t rows, cols, m, n, m_pad, n_pad, ld_x, ld_a, transposed, part_cnt;
   size_t x_bytes, a_bytes, part_bytes;
 };
 
@@ -64,11 +64,13 @@ Geometry geometry_of(const muon_shape_t& s) {
   g.m_pad = (int32_t)round_up(g.m, NS_PAD_M);
   g.n_pad = (int32_t)round_up(g.n, NS_PAD_N);
   g.part_cnt = (int32_t)((s.rows * s.cols + MOM_CHUNK - 1) / MOM_CHUNK);
-  g.x_bytes = align_up((size_t)g.m_pad * g.n_pad * 2);
+  g.ld_x = g.n_pad + NS_LD_PAD;
+  g.ld_a = g.m_pad + NS_LD_PAD;
+  g.x_bytes = align_up((size_t)g.m_pad * g.ld_x * 2);
   // A and B carry NS_PAD_M spare rows: an update tile may hang over the last
   // rows and fetch (never store) up to UPD_BM - UPD_ROWU rows past m_pad.
   static_assert(UPD_BM - UPD_ROWU <= NS_PAD_M, "spare rows");
-  g.a_bytes = align_up((size_t)(g.m_pad + NS_PAD_M) * g.m_pad * 2);
+  g.a_bytes = align_up((size_t)(g.m_pad + NS_PAD_M) * g.ld_a * 2);
   g.part_bytes = align_up((size_t)g.part_cnt * sizeof(double));
   return g;
 }
@@ -82,7 +84,7 @@ int check_shapes(const muon_shape_t* shapes, int n) {
     if (r > (int64_t)INT32_MAX || c > (int64_t)INT32_MAX || r * c >= ((int64_t)1 << 31))
       return fail(MUON_EINVAL, "matrix %d: shape %lld x %lld has 2^31 or more elements", i, (long long)r, (long long)c);
     const Geometry g = geometry_of(shapes[i]);
-    if ((int64_t)g.m_pad * g.n_pad >= ((int64_t)1 << 31))
+    if ((int64_t)g.m_pad * g.ld_x >= ((int64_t)1 << 31) || (int64_t)(g.m_pad + NS_PAD_M) * g.ld_a >= ((int64_t)1 << 31))
       return fail(MUON_EINVAL, "matrix %d: padded shape too large", i);
   }
   return MUON_OK;
@@ -287,6 +289,8 @@ int get_plan(DeviceState& st, int mode, int n, const muon_shape_t* shapes, float
     d.n = g.n;
     d.m_pad = g.m_pad;
     d.n_pad = g.n_pad;
+    d.ld_x = g.ld_x;
+    d.ld_a = g.ld_a;
     d.transposed = g.transposed;
     d.part_cnt = g.part_cnt;
     if (mode == MODE_STEP) {

@@ -15,6 +15,10 @@ constexpr int UPD_ROWU = 64;               // UPDATE tile rows start at multiple
 constexpr int NS_PAD_M = 128;              // multiple of SYM_BM and SYM_BN
 constexpr int NS_PAD_N = 256;              // multiple of UPD_BN
 constexpr int NS_THREADS = 256;
+// Row strides of X (n_pad + NS_LD_PAD) and of A / B (m_pad + NS_LD_PAD), in
+// elements: 128 bytes past a multiple of 512 bytes, so that the rows a tile
+// touches spread over the L2 channels instead of repeating a few of them.
+constexpr int NS_LD_PAD = 64;
 
 // Elementwise kernels.
 constexpr int EW_THREADS = 256;
@@ -39,6 +43,8 @@ struct MatDesc {
   int32_t transposed;     // 1 when rows > cols
   int32_t part_cnt;
   int32_t vec4;           // 1 when every row start allows 4-element vector access
+  int32_t ld_x;           // row stride of X[0], X[1] (elements)
+  int32_t ld_a;           // row stride of A and B (elements)
   int32_t pad_;
 };
 
