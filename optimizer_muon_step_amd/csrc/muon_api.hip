@@ -305,6 +305,10 @@ int get_plan(DeviceState& st, int mode, int n, const muon_shape_t* shapes, float
     const int at = ((g.rows + CAST_TILE - 1) / CAST_TILE) * ((g.cols + CAST_TILE - 1) / CAST_TILE);
     for (int t = 0; t < at; ++t) apply.push_back({i, t});
   }
+  // The cast re-reads what the momentum pass just streamed: walking it
+  // backwards starts with the lines most likely still in the memory-side
+  // cache.
+  std::reverse(cast.begin(), cast.end());
   // GEMM tiles.  Per matrix in an order that reuses operands (update: all row
   // tiles of one column block in a row, sharing that block of X; symmetric
   // phases: upper-triangle tiles row by row), then spread over the XCDs.
