@@ -194,6 +194,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const M
       b_vo[p] = 0;  // k-major: the swizzle depends on more than g % 2, computed per instruction
     }
   }
+  // A diagonal tile of a symmetric product multiplies a row block by itself:
+  // its B operand is the A slice already in LDS, fetched once.  (Only with
+  // two stages, whose waits drain everything; a deeper ring counts transfers.)
+  const bool same_rows = !NN && NSTAGE == 2 && row0 == col0;
   auto issue = [&](int s) {
     const int kt = kt_of(s);
     LDS_AS char* st = (LDS_AS char*)lds + (s % NSTAGE) * STAGE_BYTES;
@@ -203,6 +207,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const M
       const uint16_t* src_row = Aop + (int64_t)(row0 + g * 8) * lda + (int64_t)kt * BK;
       __builtin_amdgcn_global_load_lds((const void*)(src_row + a_vo[g & 1]), (LDS_AS void*)(st + g * 1024), 16, 0, 0);
     }
+    if (same_rows) return;
 #pragma unroll
     for (int q = 0; q < B_INSTR; ++q) {
       const int g = wave * B_INSTR + q;
@@ -240,7 +245,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const M
   for (int nj = 0; nj < TN; ++nj) {
     if (!NN) {
       const int r = wj * WTN + nj * 32 + (lane & 31);
-      b_rd[nj][0] = A_BYTES + r * 128 + swz_k(r, lane >> 5) * 16;
+      b_rd[nj][0] = (same_rows ? 0 : A_BYTES) + r * 128 + swz_k(r, lane >> 5) * 16;
       b_rd[nj][1] = 0;
     } else {
       const int g = (lane >> 4) & 3, l16 = lane & 15;
