@@ -204,26 +204,32 @@ int acquire_workspace(DeviceState& st, size_t need, hipStream_t stream) {
 // Workgroup w of a launch runs on XCD w % kXcds, and each XCD has its own L2.
 // Cut the locality-ordered tile sequence into kXcds contiguous runs of about
 // equal cost and interleave them, so that each XCD works through one run and
-// its concurrently resident tiles share operands in that XCD's L2.  Runs of
-// unequal length are padded with empty items (mat = -1) that exit at once.
+// its concurrently resident tiles share operands in that XCD's L2.  Within a
+// run, tiles are dispatched longest first (stable, so tiles of equal cost
+// keep their locality order): the short ones then fill the gaps at the end
+// instead of a long tile starting last.  Runs of unequal length are padded
+// with empty items (mat = -1) that exit at once.
 constexpr int kXcds = 8;
 
 std::vector<GemmItem> xcd_interleave(const std::vector<GemmItem>& seq, const std::vector<int64_t>& cost) {
   int64_t total = 0;
   for (int64_t c : cost) total += c;
-  std::vector<std::vector<GemmItem>> run(kXcds);
+  std::vector<std::vector<std::pair<int64_t, GemmItem>>> run(kXcds);
   int64_t acc = 0;
   int x = 0;
   for (size_t k = 0; k < seq.size(); ++k) {
     while (x < kXcds - 1 && acc >= total * (x + 1) / kXcds) ++x;
-    run[x].push_back(seq[k]);
+    run[x].push_back({cost[k], seq[k]});
     acc += cost[k];
   }
   size_t len = 0;
-  for (auto& r : run) len = std::max(len, r.size());
+  for (auto& r : run) {
+    std::stable_sort(r.begin(), r.end(), [](const auto& a, const auto& b) { return a.first > b.first; });
+    len = std::max(len, r.size());
+  }
   std::vector<GemmItem> out(len * kXcds, GemmItem{-1, 0, 0});
   for (int r = 0; r < kXcds; ++r)
-    for (size_t k = 0; k < run[r].size(); ++k) out[k * kXcds + r] = run[r][k];
+    for (size_t k = 0; k < run[r].size(); ++k) out[k * kXcds + r] = run[r][k].second;
   return out;
 }
 
