@@ -425,11 +425,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const M
   constexpr int ROWB = BN * 2;          // staged row bytes
   constexpr int RCH = BN / 8;           // 16-byte chunks per staged row
   static_assert(KIND == GEMM_UPDATE || BM == BN, "symmetric tiles are square");
-  static_assert((KIND == GEMM_UPDATE ? 1 : 2) * BM * ROWB <= NSTAGE * STAGE_BYTES, "staging does not fit");
-  // chunk swizzle of a staged row: spreads a column of 16-byte chunks over the banks
-  auto ech = [&](int r, int c) { return c ^ (r & (RCH - 1) & 31); };
+  static_assert(BM * ROWB <= NSTAGE * STAGE_BYTES, "staging does not fit");
+  static_assert(RCH >= 16, "staging swizzle needs 16 chunks per row");
+  // Chunk swizzle of a staged row.  Copy-out reads 16 lanes along one row
+  // (any XOR keeps them distinct); the transposing reads of the mirror put a
+  // 32-lane half on 4 consecutive rows and 4 consecutive chunks, which the
+  // XOR by 4 (r % 4) sends to 4 different 64-byte bank groups.
+  auto ech = [&](int r, int c) { return c ^ (4 * (r & 3)) ^ ((r >> 2) & 3); };
   const bool diag = (KIND != GEMM_UPDATE) && (row0 == col0);
-  LDS_AS char* E2 = E + BM * ROWB;  // transposed copy (symmetric off-diagonal tiles)
 #pragma unroll
   for (int mi = 0; mi < TM; ++mi) {
 #pragma unroll
@@ -447,26 +450,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const M
 #pragma unroll
           for (int k = 0; k < 4; ++k) v[k] = (KIND == GEMM_POLY) ? cb * ev[k] + cc * v[k] : ca * ev[k] + v[k];
         }
-        uint32_t h[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) h[k] = f32_to_bf16_bits(v[k]);
-        if (!diag) {
-          *(LDS_AS u32x2*)(E + r * ROWB + ech(r, c >> 3) * 16 + (c & 7) * 2) =
-              u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-          if (KIND != GEMM_UPDATE) {
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-              *(LDS_AS uint16_t*)(E2 + (c + k) * ROWB + ech(c + k, r >> 3) * 16 + (r & 7) * 2) = (uint16_t)h[k];
-          }
-        } else {
-          // diagonal tile: the upper triangle from this value, the lower by mirroring
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const int cc2 = c + k;
-            if (r <= cc2) *(LDS_AS uint16_t*)(E + r * ROWB + ech(r, cc2 >> 3) * 16 + (cc2 & 7) * 2) = (uint16_t)h[k];
-            if (r < cc2) *(LDS_AS uint16_t*)(E + cc2 * ROWB + ech(cc2, r >> 3) * 16 + (r & 7) * 2) = (uint16_t)h[k];
-          }
-        }
+        *(LDS_AS u32x2*)(E + r * ROWB + ech(r, c >> 3) * 16 + (c & 7) * 2) =
+            u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
       }
     }
   }
@@ -475,21 +460,52 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const M
   asm volatile("" ::: "memory");
   constexpr int CHUNKS = BM * RCH;
   static_assert(CHUNKS % NT == 0, "copy-out split");
-#pragma unroll
-  for (int s = 0; s < CHUNKS / NT; ++s) {
-    const int q = tid + s * NT;
-    const int r = q / RCH, c = q % RCH;
-    const u32x4 val = *(const LDS_AS u32x4*)(E + r * ROWB + ech(r, c) * 16);
-    if (row0 + r < row_lim)
-      *reinterpret_cast<MUON_GLOBAL u32x4*>(C + (int64_t)(row0 + r) * ldc + col0 + c * 8) = val;
-  }
-  if (KIND != GEMM_UPDATE && !diag) {
+  if (!diag) {
 #pragma unroll
     for (int s = 0; s < CHUNKS / NT; ++s) {
       const int q = tid + s * NT;
       const int r = q / RCH, c = q % RCH;
-      const u32x4 val = *(const LDS_AS u32x4*)(E2 + r * ROWB + ech(r, c) * 16);
-      *reinterpret_cast<MUON_GLOBAL u32x4*>(C + (int64_t)(col0 + r) * ldc + row0 + c * 8) = val;
+      const u32x4 val = *(const LDS_AS u32x4*)(E + r * ROWB + ech(r, c) * 16);
+      if (row0 + r < row_lim)
+        *reinterpret_cast<MUON_GLOBAL u32x4*>(C + (int64_t)(row0 + r) * ldc + col0 + c * 8) = val;
+    }
+  }
+  if constexpr (KIND != GEMM_UPDATE) {
+    // Mirror (and the diagonal tile's lower triangle) from transposing reads
+    // of the staged tile: in each 16-lane group, lane L reads row k0 + L/4,
+    // columns j0 + 4 (L % 4) .. +3, and lane i receives column j0 + i, rows
+    // k0 .. k0+3; two reads give 8 rows, one 16-byte piece of a mirrored
+    // row.  Group task g covers columns j0 = 16 (g % (BN/16)), rows
+    // k0 = 8 (g / (BN/16)); the two groups of a 32-lane half share k0.
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    constexpr int NGT = (BN / 16) * (BM / 8);
+    static_assert(NGT % (NT / 16) == 0, "mirror split");
+    const int i16 = tid & 15;
+#pragma unroll
+    for (int it = 0; it < NGT / (NT / 16); ++it) {
+      const int g = it * (NT / 16) + (tid >> 4);
+      const int j0 = 16 * (g % (BN / 16)), k0 = 8 * (g / (BN / 16));
+      const int kr = k0 + (i16 >> 2), jc = j0 + 4 * (i16 & 3);
+      const LDS_AS char* p0 = E + kr * ROWB + ech(kr, jc >> 3) * 16 + (jc & 7) * 2;
+      const LDS_AS char* p1 = E + (kr + 4) * ROWB + ech(kr + 4, jc >> 3) * 16 + (jc & 7) * 2;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)p0);
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)p1);
+      u32x4 val = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      const int j = j0 + i16;  // mirrored row = staged column
+      if (diag) {
+        // row j of the diagonal tile: staged row j where it lies on or above
+        // the diagonal (column >= j), its mirror below
+        const u32x4 rm = *(const LDS_AS u32x4*)(E + j * ROWB + ech(j, k0 >> 3) * 16);
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t lo16 = (j <= k0 + 2 * e) ? (rm[e] & 0xffffu) : (val[e] & 0xffffu);
+          const uint32_t hi16 = (j <= k0 + 2 * e + 1) ? (rm[e] >> 16) : (val[e] >> 16);
+          w[e] = lo16 | (hi16 << 16);
+        }
+        val = u32x4{w[0], w[1], w[2], w[3]};
+      }
+      *reinterpret_cast<MUON_GLOBAL u32x4*>(C + (int64_t)(col0 + j) * ldc + row0 + k0) = val;
     }
   }
 }
