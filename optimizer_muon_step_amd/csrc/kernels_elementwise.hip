@@ -150,10 +150,11 @@ __device__ __forceinline__ void load4_src(const MatDesc& d, int r, int c, float 
     }
     return;
   }
+  // G and M are read here for the last time in the step: non-temporal loads
   float g[4], m[4];
   if (d.vec4 && c + 3 < d.cols) {
-    const f32x4 g4 = *reinterpret_cast<const MUON_GLOBAL f32x4*>(gptr(d.G) + off);
-    const f32x4 m4 = *reinterpret_cast<const MUON_GLOBAL f32x4*>(gptr(d.M) + off);
+    const f32x4 g4 = __builtin_nontemporal_load(reinterpret_cast<const MUON_GLOBAL f32x4*>(gptr(d.G) + off));
+    const f32x4 m4 = __builtin_nontemporal_load(reinterpret_cast<const MUON_GLOBAL f32x4*>(gptr(d.M) + off));
     g[0] = g4.x; g[1] = g4.y; g[2] = g4.z; g[3] = g4.w;
     m[0] = m4.x; m[1] = m4.y; m[2] = m4.z; m[3] = m4.w;
   } else {
