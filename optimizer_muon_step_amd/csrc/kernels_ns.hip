@@ -39,8 +39,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #define LDS_AS __attribute__((address_space(3)))
 
-constexpr int BK = 64;  // K per pipeline stage: one 128-byte line per k-contiguous row
-
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] + vmcnt_hi[15:14],
 // expcnt[6:4], lgkmcnt[11:8]): wait until at most n vector-memory operations
 // are outstanding and every LDS operation has completed.
@@ -51,10 +49,16 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(n));
 }
 
-// k-contiguous tile: rows of 128 B (8 chunks of 16 B).  A fragment read has
-// 16 lanes on 16 consecutive rows at one chunk; two rows share a 256-byte
-// bank line, so XOR by (r/2)%8 sends the 16 reads to 16 distinct chunks.
-__device__ __forceinline__ int swz_k(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+// k-contiguous tile, K slice of BK elements: rows of 2 BK bytes.  A fragment
+// read has 16 lanes on 16 consecutive rows at one 16-byte chunk.  128-byte
+// rows (BK 64, 8 chunks): two rows share a 256-byte bank line, so XOR by
+// (r/2)%8.  64-byte rows (BK 32, 4 chunks): four rows share one, so XOR by
+// (r/4)%4.  Either way the 16 reads land on 16 distinct chunks.
+template <int BK>
+__device__ __forceinline__ int swz_k(int row, int chunk) {
+  static_assert(BK == 64 || BK == 32, "k-contiguous rows of 64 or 128 bytes");
+  return BK == 64 ? chunk ^ ((row >> 1) & 7) : chunk ^ ((row >> 2) & 3);
+}
 // k-major tile: rows of BN*2 bytes.  A transposing read has each 16-lane
 // group on 4 consecutive rows, 32 bytes each, and pairs of groups 32 bytes
 // apart; XOR by 4(r%4) moves the 4 rows into different 64-byte bank groups.
@@ -110,7 +114,7 @@ __device__ __forceinline__ void read_tr_frags4(bf16x8* bfr, const uint32_t* a) {
 
 }  // namespace
 
-template <int KIND, int BM, int BN, int WAVES_M, int WAVES_N, int NSTAGE, int ROWU>
+template <int KIND, int BM, int BN, int WAVES_M, int WAVES_N, int NSTAGE, int ROWU, int BK>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const MatDesc* __restrict__ descs,
                                                                         const GemmItem* __restrict__ items,
                                                                         int src, float ca, float cb, float cc) {
@@ -124,13 +128,17 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const M
   constexpr int B_INSTR = B_BYTES / (16 * NT);
   constexpr int LPW = A_INSTR + B_INSTR;
   constexpr int NCHUNK_N = BN / 8;  // chunks per k-major row
+  constexpr int RB = BK * 2;        // bytes per k-contiguous row of a slice
+  constexpr int CPR = BK / 8;       // 16-byte chunks per k-contiguous row
+  constexpr int RPI = 1024 / RB;    // k-contiguous rows per wave DMA instruction
   // UPDATE: K slices holding the tile's own rows, and the ones kept past the
   // two stage buffers so that all of them are in LDS when the loop ends.
   constexpr int OWN = NN ? BM / BK : 0;
   constexpr int EXTRA = (OWN > 2) ? OWN - 2 : 0;
   static_assert(A_INSTR >= 1 && B_INSTR >= 1 && A_INSTR * 16 * NT == A_BYTES && B_INSTR * 16 * NT == B_BYTES,
                 "tile does not split into whole DMA instructions");
-  static_assert(NSTAGE >= 2 && NSTAGE <= 3 && TM >= 1 && TN >= 1, "unsupported tile");
+  static_assert(NSTAGE >= 2 && NSTAGE <= 4 && TM >= 1 && TN >= 1, "unsupported tile");
+  static_assert(!NN || BK == 64, "the k-major X slice is read 64 rows at a time");
   static_assert(!NN || ((TN == 2 || TN == 4) && BM % BK == 0 && OWN <= 3 && ROWU == BK && (NSTAGE == 2 || OWN <= 2)),
                 "UPDATE tiling: tile rows a whole number (<= 3) of K slices, kept in the ring or aside");
   static_assert(NN || ROWU == BM, "symmetric tiles are addressed in units of their own size");
@@ -184,27 +192,28 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const M
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     {
-      const int row = p * 8 + (lane >> 3);  // row within a pair of instructions
-      a_vo[p] = (lane >> 3) * lda + swz_k(row, lane & 7) * 8;
+      // the swizzle repeats every 16 rows: 2 instructions of 8 rows (BK 64)
+      // or 1 of 16 (BK 32), so instruction parity p is all it needs
+      const int row = p * RPI + lane / CPR;
+      a_vo[p] = (lane / CPR) * lda + swz_k<BK>(row, lane % CPR) * 8;
     }
     if (!NN) {
-      const int row = p * 8 + (lane >> 3);
-      b_vo[p] = (lane >> 3) * ldb + swz_k(row, lane & 7) * 8;
+      const int row = p * RPI + lane / CPR;
+      b_vo[p] = (lane / CPR) * ldb + swz_k<BK>(row, lane % CPR) * 8;
     } else {
       b_vo[p] = 0;  // k-major: the swizzle depends on more than g % 2, computed per instruction
     }
   }
   // A diagonal tile of a symmetric product multiplies a row block by itself:
-  // its B operand is the A slice already in LDS, fetched once.  (Only with
-  // two stages, whose waits drain everything; a deeper ring counts transfers.)
-  const bool same_rows = !NN && NSTAGE == 2 && row0 == col0;
+  // its B operand is the A slice already in LDS, fetched once.
+  const bool same_rows = !NN && row0 == col0;
   auto issue = [&](int s) {
     const int kt = kt_of(s);
     LDS_AS char* st = (LDS_AS char*)lds + (s % NSTAGE) * STAGE_BYTES;
 #pragma unroll
     for (int q = 0; q < A_INSTR; ++q) {
       const int g = wave * A_INSTR + q;
-      const uint16_t* src_row = Aop + (int64_t)(row0 + g * 8) * lda + (int64_t)kt * BK;
+      const uint16_t* src_row = Aop + (int64_t)(row0 + g * RPI) * lda + (int64_t)kt * BK;
       __builtin_amdgcn_global_load_lds((const void*)(src_row + a_vo[g & 1]), (LDS_AS void*)(st + g * 1024), 16, 0, 0);
     }
     if (same_rows) return;
@@ -218,7 +227,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const M
         src_row = Bop + (int64_t)(kt * BK + g * (64 / NCHUNK_N)) * ldb + col0;
         vo = (lane / NCHUNK_N) * ldb + swz_n(row, lane % NCHUNK_N) * 8;
       } else {
-        src_row = Bop + (int64_t)(col0 + g * 8) * ldb + (int64_t)kt * BK;
+        src_row = Bop + (int64_t)(col0 + g * RPI) * ldb + (int64_t)kt * BK;
         vo = b_vo[g & 1];
       }
       __builtin_amdgcn_global_load_lds((const void*)(src_row + vo), (LDS_AS void*)(st + A_BYTES + g * 1024), 16, 0, 0);
@@ -239,13 +248,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const M
 #pragma unroll
   for (int mi = 0; mi < TM; ++mi) {
     const int r = wi * WTM + mi * 32 + (lane & 31);
-    a_rd[mi] = r * 128 + swz_k(r, lane >> 5) * 16;
+    a_rd[mi] = r * RB + swz_k<BK>(r, lane >> 5) * 16;
   }
 #pragma unroll
   for (int nj = 0; nj < TN; ++nj) {
     if (!NN) {
       const int r = wj * WTN + nj * 32 + (lane & 31);
-      b_rd[nj][0] = (same_rows ? 0 : A_BYTES) + r * 128 + swz_k(r, lane >> 5) * 16;
+      b_rd[nj][0] = (same_rows ? 0 : A_BYTES) + r * RB + swz_k<BK>(r, lane >> 5) * 16;
       b_rd[nj][1] = 0;
     } else {
       const int g = (lane >> 4) & 3, l16 = lane & 15;
@@ -352,7 +361,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const M
         for (int e4 = 0; e4 < 4; ++e4) {
           const int ar = wi * WTM + mi * 32 + (lane & 31);
           const int kl = cbase % BK + 8 * e4 + 4 * (lane >> 5);
-          ein[mi][nj][e4] = *(const LDS_AS u32x2*)(st + ar * 128 + swz_k(ar, kl >> 3) * 16 + (kl & 7) * 2);
+          ein[mi][nj][e4] = *(const LDS_AS u32x2*)(st + ar * RB + swz_k<BK>(ar, kl >> 3) * 16 + (kl & 7) * 2);
         }
     }
   };
@@ -378,10 +387,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const M
   for (int s = 0; s < NSTAGE - 1; ++s)
     if (s < KT) issue(s);
   for (int s = 0; s < KT; ++s) {
-    if (NSTAGE == 3 && s + 1 < KT)
-      wait_vm_lgkm0<LPW>();
-    else
+    // slices issued after s: min(NSTAGE - 2, KT - 1 - s), each LPW transfers
+    // per wave (A_INSTR on a diagonal tile, which fetches one operand)
+    const int after = min(NSTAGE - 2, KT - 1 - s);
+    if (after >= 2 && NSTAGE >= 4) {
+      if (same_rows) wait_vm_lgkm0<2 * A_INSTR>(); else wait_vm_lgkm0<2 * LPW>();
+    } else if (after >= 1 && NSTAGE >= 3) {
+      if (same_rows) wait_vm_lgkm0<A_INSTR>(); else wait_vm_lgkm0<LPW>();
+    } else {
       wait_vm_lgkm0<0>();
+    }
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if (s + NSTAGE - 1 < KT) issue(s + NSTAGE - 1);
@@ -515,13 +530,13 @@ hipError_t launch_gemm(int kind, const MatDesc* d, const GemmItem* items, int n_
   if (n_items == 0) return hipSuccess;
   switch (kind) {
     case GEMM_GRAM:
-      ns_gemm_kernel<GEMM_GRAM, SYM_BM, SYM_BN, 2, 2, 2, SYM_BM><<<n_items, 256, 0, s>>>(d, items, src, ca, cb, cc);
+      ns_gemm_kernel<GEMM_GRAM, SYM_BM, SYM_BN, 2, 2, SYM_NSTAGE, SYM_BM, SYM_BK><<<n_items, 256, 0, s>>>(d, items, src, ca, cb, cc);
       break;
     case GEMM_POLY:
-      ns_gemm_kernel<GEMM_POLY, SYM_BM, SYM_BN, 2, 2, 2, SYM_BM><<<n_items, 256, 0, s>>>(d, items, src, ca, cb, cc);
+      ns_gemm_kernel<GEMM_POLY, SYM_BM, SYM_BN, 2, 2, SYM_NSTAGE, SYM_BM, SYM_BK><<<n_items, 256, 0, s>>>(d, items, src, ca, cb, cc);
       break;
     default:
-      ns_gemm_kernel<GEMM_UPDATE, UPD_BM, UPD_BN, 2, 4, 2, UPD_ROWU><<<n_items, 512, 0, s>>>(d, items, src, ca, cb, cc);
+      ns_gemm_kernel<GEMM_UPDATE, UPD_BM, UPD_BN, 2, 4, 2, UPD_ROWU, 64><<<n_items, 512, 0, s>>>(d, items, src, ca, cb, cc);
       break;
   }
   return hipGetLastError();

@@ -10,6 +10,7 @@ namespace muon {
 // canonical m is padded to NS_PAD_M and n to NS_PAD_N, with the padding held
 // at exact zero, so the GEMM kernels never bounds-check.
 constexpr int SYM_BM = 128, SYM_BN = 128;  // GRAM / POLY output tile
+constexpr int SYM_BK = 64, SYM_NSTAGE = 2;  // GRAM / POLY K slice and ring depth (measured best)
 constexpr int UPD_BM = 192, UPD_BN = 256;  // UPDATE output tile (rows may overhang m_pad)
 constexpr int UPD_ROWU = 64;               // UPDATE tile rows start at multiples of this
 constexpr int NS_PAD_M = 128;              // multiple of SYM_BM and SYM_BN
