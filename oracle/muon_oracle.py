@@ -34,7 +34,11 @@ Readings taken where the pages are silent (each one is a choice, not a quote):
                           rounding per operation and no fused multiply-add
   R6 coefficients         one (a, b, c) triple for every iteration, default
                           (3.4445, -4.7750, 2.0315); these values are not
-                          printed on the pages
+                          printed on the pages.  Or a schedule: one triple per
+                          iteration, triple k used in iteration k (tweet 6/8
+                          presents the coefficients as a trade-off between
+                          slope at zero and closeness to 1; choosing them per
+                          iteration is the plain extension of that choice)
   R7 apply                W <- W - lr * O with no extra scale and no weight
                           decay (the thread's replies report weight decay as
                           worse), rounded once per operation in fp32
@@ -138,11 +142,21 @@ def ns_iteration(X, a, b, c, mode="emul"):
     return bf16_round((fa * X) + BX)
 
 
+def coefficient_schedule(coeffs, ns_steps):
+    """Reading R6: the (a, b, c) used in each iteration.  `coeffs` is one
+    triple (used every time) or ns_steps triples (triple k in iteration k)."""
+    arr = np.asarray(coeffs, dtype=np.float64)
+    if arr.shape == (3,):
+        return [tuple(float(v) for v in arr)] * ns_steps
+    if arr.shape == (ns_steps, 3):
+        return [tuple(float(v) for v in row) for row in arr]
+    raise ValueError(f"coeffs must be one triple or {ns_steps} triples, got shape {arr.shape}")
+
+
 def newton_schulz(X0, ns_steps, coeffs=DEFAULT_COEFFS, mode="emul"):
     """ns_steps iterations on a canonical (m <= n) matrix; returns the final X."""
-    a, b, c = coeffs
     X = X0
-    for _ in range(ns_steps):
+    for a, b, c in coefficient_schedule(coeffs, ns_steps):
         X = ns_iteration(X, a, b, c, mode)
     return X
 

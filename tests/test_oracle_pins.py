@@ -447,3 +447,82 @@ def test_mutations_are_caught(monkeypatch):
     monkeypatch.setattr(om, "ns_iteration", b_not_rounded)
     with pytest.raises(AssertionError):
         test_monomial_inputs_bit_exact((12, 20), False)
+
+
+# ------------------------------------------------- coefficient schedules --
+# One (a, b, c) per iteration.  In exact arithmetic the iteration still acts
+# on each singular value separately, now through the composition of the
+# per-iteration polynomials, in iteration order.
+
+SCHEDULE = [(3.4445, -4.7750, 2.0315), (3.0, -3.2, 1.2), (2.5, -2.0, 0.6), (2.0, -1.5, 0.5),
+            (1.875, -1.25, 0.375)]
+
+
+def p_composed(sig, schedule):
+    for coeffs in schedule:
+        sig = p_scalar(sig, 1, coeffs)
+    return sig
+
+
+@pytest.mark.parametrize("shape", [(12, 20), (16, 16), (24, 40)])
+def test_schedule_singular_value_closed_form(shape):
+    rng = np.random.default_rng(41)
+    g = rng.standard_normal(shape)
+    O = om.orthogonalize(g, len(SCHEDULE), SCHEDULE, mode="exact")[0]
+    U, sig, Vt = np.linalg.svd(g / (np.linalg.norm(g) + om.NORM_EPS), full_matrices=False)
+    assert rel_f(O, (U * p_composed(sig, SCHEDULE)) @ Vt) < 1e-8
+
+
+def test_schedule_order_matters():
+    """The reversed schedule is a different map: a slip that applied the
+    triples in the wrong order would fail the closed form above."""
+    rng = np.random.default_rng(42)
+    g = rng.standard_normal((12, 20))
+    fwd = om.orthogonalize(g, len(SCHEDULE), SCHEDULE, mode="exact")[0]
+    rev = om.orthogonalize(g, len(SCHEDULE), SCHEDULE[::-1], mode="exact")[0]
+    assert rel_f(fwd, rev) > 1e-3
+
+
+def test_schedule_of_equal_triples_is_the_fixed_triple():
+    """emul mode, bit for bit: a schedule repeating the default triple is the
+    default iteration."""
+    rng = np.random.default_rng(43)
+    X0 = om.bf16_round(rng.standard_normal((20, 36)).astype(np.float32) * np.float32(0.05))
+    a = om.newton_schulz(X0, 4, COEFFS)
+    b = om.newton_schulz(X0, 4, [COEFFS] * 4)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_schedule_rank_one_scalar_chain():
+    """Rank 1 (normalised sigma = 1 up to eps): O = f(1) u v^T with f the
+    composed polynomial, computed by hand here."""
+    rng = np.random.default_rng(44)
+    u = rng.standard_normal(9)
+    v = rng.standard_normal(15)
+    g = np.outer(u, v)
+    O = om.orthogonalize(g, len(SCHEDULE), SCHEDULE, mode="exact")[0]
+    sigma = np.linalg.norm(g) / (np.linalg.norm(g) + om.NORM_EPS)
+    s = sigma
+    for a, b, c in SCHEDULE:
+        s = a * s + b * s ** 3 + c * s ** 5
+    want = s * np.outer(u / np.linalg.norm(u), v / np.linalg.norm(v))
+    assert rel_f(O, want) < 1e-12
+
+
+def test_textbook_quintic_schedule_reaches_the_polar_factor():
+    """With every triple (15/8, -10/8, 3/8), the textbook quintic
+    Newton-Schulz polar iteration (p(1) = 1, p'(1) = p''(1) = 0), the
+    iterate converges to U V^T, the orthogonal polar factor of the input."""
+    rng = np.random.default_rng(45)
+    Q1, _ = np.linalg.qr(rng.standard_normal((10, 10)))
+    Q2, _ = np.linalg.qr(rng.standard_normal((16, 10)))
+    sig = np.linspace(0.2, 1.0, 10)          # condition number 5
+    g = (Q1 * sig) @ Q2.T                      # 10 x 16
+    O = om.orthogonalize(g, 20, [(1.875, -1.25, 0.375)] * 20, mode="exact")[0]
+    U, _, Vt = np.linalg.svd(g, full_matrices=False)
+    assert rel_f(O, U @ Vt) < 1e-12
+
+
+def test_schedule_shape_is_checked():
+    with pytest.raises(ValueError):
+        om.newton_schulz(np.zeros((4, 6), np.float32), 3, [COEFFS] * 2)
