@@ -97,6 +97,19 @@ int muon_step_ex(float* const* params, const float* const* grads, float* const* 
                  const float* coeffs, uint16_t* const* updates, hipStream_t stream);
 
 /*
+ * muon_step_ex with a coefficient schedule: coeffs is a host array of
+ * 3 * ns_steps floats, iteration k (0-based) using coeffs[3k .. 3k+2] as
+ * {a, b, c}; all must be finite; it may be NULL when ns_steps = 0.  (The
+ * thread's tweet 6/8 presents the coefficients as a trade-off between the
+ * slope at zero and closeness to 1; a schedule makes that choice per
+ * iteration.)  A schedule repeating one triple gives exactly muon_step_ex's
+ * result.  updates as in muon_step_ex (may be NULL).
+ */
+int muon_step_sched(float* const* params, const float* const* grads, float* const* momentum,
+                    const muon_shape_t* shapes, int n, float lr, float beta, int ns_steps,
+                    const float* coeffs, uint16_t* const* updates, hipStream_t stream);
+
+/*
  * The Newton-Schulz core alone: out[i] = iterate(x[i]) with the same
  * storage points as muon_step, no normalisation, no momentum.  x[i] and out[i]
  * are bf16 bit patterns (uint16), rows x cols in the caller's orientation
@@ -105,6 +118,11 @@ int muon_step_ex(float* const* params, const float* const* grads, float* const* 
  */
 int muon_newton_schulz(const uint16_t* const* x, uint16_t* const* out, const muon_shape_t* shapes,
                        int n, int ns_steps, const float* coeffs, hipStream_t stream);
+
+/* muon_newton_schulz with a coefficient schedule (3 * ns_steps floats, as in
+ * muon_step_sched). */
+int muon_newton_schulz_sched(const uint16_t* const* x, uint16_t* const* out, const muon_shape_t* shapes,
+                             int n, int ns_steps, const float* coeffs, hipStream_t stream);
 
 /* Thread-local description of the last failing call on this thread ("" if none). */
 const char* muon_last_error(void);

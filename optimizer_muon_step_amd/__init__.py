@@ -65,10 +65,25 @@ def _bf16_matrix(t, what):
     return t.data_ptr()
 
 
+def _coeff_arg(coeffs, ns_steps):
+    """(is a schedule, ctypes float array): one (a, b, c) for every iteration,
+    or ns_steps triples, triple k for iteration k."""
+    rows = [list(c) if hasattr(c, "__len__") else None for c in coeffs]
+    if all(r is None for r in rows):
+        vals = [float(c) for c in coeffs]
+        if len(vals) != 3:
+            raise ValueError("coeffs: expected (a, b, c) or one (a, b, c) per iteration")
+        return False, _lib.float3(vals)
+    if any(r is None or len(r) != 3 for r in rows) or len(rows) != ns_steps:
+        raise ValueError(f"coeffs schedule: expected {ns_steps} triples (a, b, c)")
+    return True, _lib.float_array([float(v) for r in rows for v in r])
+
+
 def muon_step(params, grads, momentum, lr=0.02, beta=0.95, ns_steps=5, coeffs=DEFAULT_COEFFS,
               updates=None, stream=None) -> None:
     """One Muon step over lists of 2-D fp32 tensors (params and momentum updated in place).
-    `updates`, if given, is a list of bf16 tensors (or None entries) receiving the applied update."""
+    `coeffs` is one (a, b, c) or a schedule of ns_steps triples.  `updates`, if
+    given, is a list of bf16 tensors (or None entries) receiving the applied update."""
     n = len(params)
     if len(grads) != n or len(momentum) != n:
         raise ValueError("params, grads and momentum must have the same length")
@@ -83,10 +98,13 @@ def muon_step(params, grads, momentum, lr=0.02, beta=0.95, ns_steps=5, coeffs=DE
     G = _lib.ptr_array([g.data_ptr() for g in grads])
     M = _lib.ptr_array([m.data_ptr() for m in momentum])
     S = _lib.shape_array(shapes)
-    C = _lib.float3(coeffs)
+    sched, C = _coeff_arg(coeffs, ns_steps)
     st = ctypes.c_void_p(_stream_handle(stream))
     if updates is None:
-        rc = lib.muon_step(P, G, M, S, n, float(lr), float(beta), int(ns_steps), C, st)
+        if sched:
+            rc = lib.muon_step_sched(P, G, M, S, n, float(lr), float(beta), int(ns_steps), C, None, st)
+        else:
+            rc = lib.muon_step(P, G, M, S, n, float(lr), float(beta), int(ns_steps), C, st)
     else:
         if len(updates) != n:
             raise ValueError("updates must have one entry per matrix")
@@ -100,12 +118,14 @@ def muon_step(params, grads, momentum, lr=0.02, beta=0.95, ns_steps=5, coeffs=DE
                 raise ValueError(f"updates[{i}]: shape differs from params[{i}]")
             ptrs.append(u.data_ptr())
         U = _lib.ptr_array(ptrs)
-        rc = lib.muon_step_ex(P, G, M, S, n, float(lr), float(beta), int(ns_steps), C, U, st)
+        entry = lib.muon_step_sched if sched else lib.muon_step_ex
+        rc = entry(P, G, M, S, n, float(lr), float(beta), int(ns_steps), C, U, st)
     _check(rc)
 
 
 def muon_newton_schulz(xs, outs, ns_steps=5, coeffs=DEFAULT_COEFFS, stream=None) -> None:
-    """The Newton-Schulz core alone on bf16 matrices (no normalisation)."""
+    """The Newton-Schulz core alone on bf16 matrices (no normalisation);
+    `coeffs` is one (a, b, c) or a schedule of ns_steps triples."""
     n = len(xs)
     if len(outs) != n:
         raise ValueError("xs and outs must have the same length")
@@ -116,10 +136,10 @@ def muon_newton_schulz(xs, outs, ns_steps=5, coeffs=DEFAULT_COEFFS, stream=None)
             raise ValueError(f"matrix {i}: shapes differ")
         shapes.append(tuple(x.shape))
     lib = _lib.load()
-    rc = lib.muon_newton_schulz(_lib.ptr_array([x.data_ptr() for x in xs]),
-                                _lib.ptr_array([o.data_ptr() for o in outs]),
-                                _lib.shape_array(shapes), n, int(ns_steps), _lib.float3(coeffs),
-                                ctypes.c_void_p(_stream_handle(stream)))
+    sched, C = _coeff_arg(coeffs, ns_steps)
+    entry = lib.muon_newton_schulz_sched if sched else lib.muon_newton_schulz
+    rc = entry(_lib.ptr_array([x.data_ptr() for x in xs]), _lib.ptr_array([o.data_ptr() for o in outs]),
+               _lib.shape_array(shapes), n, int(ns_steps), C, ctypes.c_void_p(_stream_handle(stream)))
     _check(rc)
 
 

@@ -99,11 +99,15 @@ size_t workspace_bytes_of(const muon_shape_t* shapes, int n) {
   return total;
 }
 
-int check_coeffs(const float* coeffs, int ns_steps) {
+// Coefficients: one {a, b, c} for every iteration (stride 0, always required),
+// or a schedule of ns_steps triples (stride 3; may be NULL when ns_steps = 0).
+int check_coeffs(const float* coeffs, int ns_steps, int stride) {
   if (ns_steps < 0 || ns_steps > MUON_MAX_NS_STEPS)
     return fail(MUON_EINVAL, "ns_steps = %d outside [0, %d]", ns_steps, MUON_MAX_NS_STEPS);
+  const int count = stride ? 3 * ns_steps : 3;
+  if (count == 0) return MUON_OK;
   if (!coeffs) return fail(MUON_EINVAL, "coeffs is NULL");
-  for (int k = 0; k < 3; ++k)
+  for (int k = 0; k < count; ++k)
     if (!std::isfinite(coeffs[k])) return fail(MUON_EINVAL, "coeffs[%d] is not finite", k);
   return MUON_OK;
 }
@@ -416,7 +420,7 @@ int timed(int kind, hipStream_t stream, F&& launch, const char* what) {
 
 int run(int mode, float* const* params, const float* const* grads, float* const* moms,
         uint16_t* const* upd, const uint16_t* const* xin, const muon_shape_t* shapes, int n, float lr,
-        float beta, int ns_steps, const float* coeffs, hipStream_t stream) {
+        float beta, int ns_steps, const float* coeffs, int stride, hipStream_t stream) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
@@ -426,7 +430,6 @@ int run(int mode, float* const* params, const float* const* grads, float* const*
   if (rc) return rc;
   Plan* p = nullptr;
   if ((rc = get_plan(st, mode, n, shapes, params, grads, moms, upd, xin, stream, &p))) return rc;
-  const float ca = coeffs[0], cb = coeffs[1], cc = coeffs[2];
   if (mode == MODE_STEP) {
     rc = timed(MUON_KERNEL_MOMENTUM, stream, [&] { return launch_momentum(p->d_desc, p->d_mom, p->n_mom, n, beta, stream); },
                "momentum kernel launch");
@@ -438,6 +441,8 @@ int run(int mode, float* const* params, const float* const* grads, float* const*
   if (rc) return rc;
   for (int k = 0; k < ns_steps; ++k) {
     const int src = k & 1;
+    const float* ck = coeffs + (size_t)k * stride;  // iteration k's a, b, c
+    const float ca = ck[0], cb = ck[1], cc = ck[2];
     rc = timed(MUON_KERNEL_GRAM, stream,
                [&] { return launch_gemm(GEMM_GRAM, p->d_desc, p->d_gram, p->n_gram, src, ca, cb, cc, stream); },
                "gram kernel launch");
@@ -458,13 +463,13 @@ int run(int mode, float* const* params, const float* const* grads, float* const*
 }
 
 int validate_step(float* const* params, const float* const* grads, float* const* moms, const muon_shape_t* shapes,
-                  int n, float lr, float beta, int ns_steps, const float* coeffs, uint16_t* const* upd) {
+                  int n, float lr, float beta, int ns_steps, const float* coeffs, int stride, uint16_t* const* upd) {
   int rc = check_shapes(shapes, n);
   if (rc) return rc;
   if (!params || !grads || !moms) return fail(MUON_EINVAL, "params, grads and momentum arrays must not be NULL");
   if (!std::isfinite(lr)) return fail(MUON_EINVAL, "lr is not finite");
   if (!std::isfinite(beta) || beta < 0.0f || beta >= 1.0f) return fail(MUON_EINVAL, "beta = %g outside [0, 1)", (double)beta);
-  if ((rc = check_coeffs(coeffs, ns_steps))) return rc;
+  if ((rc = check_coeffs(coeffs, ns_steps, stride))) return rc;
   std::vector<Range> r;
   r.reserve(4 * (size_t)n);
   for (int i = 0; i < n; ++i) {
@@ -484,32 +489,23 @@ int validate_step(float* const* params, const float* const* grads, float* const*
   return check_ranges(r);
 }
 
-}  // namespace
-
-extern "C" {
-
-int muon_step_ex(float* const* params, const float* const* grads, float* const* momentum,
-                 const muon_shape_t* shapes, int n, float lr, float beta, int ns_steps, const float* coeffs,
-                 uint16_t* const* updates, hipStream_t stream) {
+int step_entry(float* const* params, const float* const* grads, float* const* momentum, const muon_shape_t* shapes,
+               int n, float lr, float beta, int ns_steps, const float* coeffs, int stride, uint16_t* const* updates,
+               hipStream_t stream) {
   g_error.clear();
-  int rc = validate_step(params, grads, momentum, shapes, n, lr, beta, ns_steps, coeffs, updates);
+  int rc = validate_step(params, grads, momentum, shapes, n, lr, beta, ns_steps, coeffs, stride, updates);
   if (rc || n == 0) return rc;
-  return run(MODE_STEP, params, grads, momentum, updates, nullptr, shapes, n, lr, beta, ns_steps, coeffs, stream);
+  return run(MODE_STEP, params, grads, momentum, updates, nullptr, shapes, n, lr, beta, ns_steps, coeffs, stride,
+             stream);
 }
 
-int muon_step(float* const* params, const float* const* grads, float* const* momentum,
-              const muon_shape_t* shapes, int n, float lr, float beta, int ns_steps, const float* coeffs,
-              hipStream_t stream) {
-  return muon_step_ex(params, grads, momentum, shapes, n, lr, beta, ns_steps, coeffs, nullptr, stream);
-}
-
-int muon_newton_schulz(const uint16_t* const* x, uint16_t* const* out, const muon_shape_t* shapes, int n,
-                       int ns_steps, const float* coeffs, hipStream_t stream) {
+int ns_entry(const uint16_t* const* x, uint16_t* const* out, const muon_shape_t* shapes, int n, int ns_steps,
+             const float* coeffs, int stride, hipStream_t stream) {
   g_error.clear();
   int rc = check_shapes(shapes, n);
   if (rc) return rc;
   if (!x || !out) return fail(MUON_EINVAL, "x and out arrays must not be NULL");
-  if ((rc = check_coeffs(coeffs, ns_steps))) return rc;
+  if ((rc = check_coeffs(coeffs, ns_steps, stride))) return rc;
   std::vector<Range> r;
   for (int i = 0; i < n; ++i) {
     if (!x[i] || !out[i]) return fail(MUON_EINVAL, "x[%d] or out[%d] is NULL", i, i);
@@ -520,7 +516,39 @@ int muon_newton_schulz(const uint16_t* const* x, uint16_t* const* out, const muo
   }
   if ((rc = check_ranges(r))) return rc;
   if (n == 0) return MUON_OK;
-  return run(MODE_NS, nullptr, nullptr, nullptr, out, x, shapes, n, 0.0f, 0.0f, ns_steps, coeffs, stream);
+  return run(MODE_NS, nullptr, nullptr, nullptr, out, x, shapes, n, 0.0f, 0.0f, ns_steps, coeffs, stride, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int muon_step_ex(float* const* params, const float* const* grads, float* const* momentum,
+                 const muon_shape_t* shapes, int n, float lr, float beta, int ns_steps, const float* coeffs,
+                 uint16_t* const* updates, hipStream_t stream) {
+  return step_entry(params, grads, momentum, shapes, n, lr, beta, ns_steps, coeffs, 0, updates, stream);
+}
+
+int muon_step(float* const* params, const float* const* grads, float* const* momentum,
+              const muon_shape_t* shapes, int n, float lr, float beta, int ns_steps, const float* coeffs,
+              hipStream_t stream) {
+  return step_entry(params, grads, momentum, shapes, n, lr, beta, ns_steps, coeffs, 0, nullptr, stream);
+}
+
+int muon_step_sched(float* const* params, const float* const* grads, float* const* momentum,
+                    const muon_shape_t* shapes, int n, float lr, float beta, int ns_steps, const float* coeffs,
+                    uint16_t* const* updates, hipStream_t stream) {
+  return step_entry(params, grads, momentum, shapes, n, lr, beta, ns_steps, coeffs, 3, updates, stream);
+}
+
+int muon_newton_schulz(const uint16_t* const* x, uint16_t* const* out, const muon_shape_t* shapes, int n,
+                       int ns_steps, const float* coeffs, hipStream_t stream) {
+  return ns_entry(x, out, shapes, n, ns_steps, coeffs, 0, stream);
+}
+
+int muon_newton_schulz_sched(const uint16_t* const* x, uint16_t* const* out, const muon_shape_t* shapes, int n,
+                             int ns_steps, const float* coeffs, hipStream_t stream) {
+  return ns_entry(x, out, shapes, n, ns_steps, coeffs, 3, stream);
 }
 
 const char* muon_last_error(void) { return g_error.c_str(); }

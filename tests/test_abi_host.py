@@ -101,6 +101,41 @@ def test_newton_schulz_entry_validation(lib):
     assert "aligned" in lib.muon_last_error().decode()
 
 
+def test_schedule_entries_validate_every_triple(lib):
+    fake = _lib.ptr_array([0x10000])
+    fake2 = _lib.ptr_array([0x20000])
+    fake3 = _lib.ptr_array([0x30000])
+    good = _lib.shape_array([(4, 4)])
+    sched = [3.4445, -4.775, 2.0315] * 4
+    bad = list(sched)
+    bad[10] = float("inf")  # iteration 3's b
+    rc = lib.muon_step_sched(fake, fake2, fake3, good, 1, 0.02, 0.95, 4, _lib.float_array(bad), None, None)
+    assert rc == -1 and "coeffs[10]" in lib.muon_last_error().decode()
+    rc = lib.muon_step_sched(fake, fake2, fake3, good, 1, 0.02, 0.95, 4, None, None, None)
+    assert rc == -1 and "coeffs" in lib.muon_last_error().decode()
+    rc = lib.muon_newton_schulz_sched(fake, fake, good, 1, 4, _lib.float_array(bad), None)
+    assert rc == -1 and "coeffs[10]" in lib.muon_last_error().decode()
+    # a schedule may be empty when there are no iterations; n = 0 needs no device
+    assert lib.muon_step_sched(fake, fake2, fake3, good, 0, 0.02, 0.95, 0, None, None, None) == 0
+    assert lib.muon_step_sched(fake, fake2, fake3, good, 0, 0.02, 0.95, 4, _lib.float_array(sched), None,
+                               None) == 0
+    # the fixed-triple entries still require their triple
+    rc = lib.muon_step(fake, fake2, fake3, good, 1, 0.02, 0.95, 0, None, None)
+    assert rc == -1 and "coeffs" in lib.muon_last_error().decode()
+
+
+def test_binding_coefficient_forms():
+    import optimizer_muon_step_amd as mu
+    sched, arr = mu._coeff_arg([(1, 2, 3), (4, 5, 6)], 2)
+    assert sched and list(arr) == [1, 2, 3, 4, 5, 6]
+    sched, arr = mu._coeff_arg((1, 2, 3), 7)
+    assert not sched and list(arr) == [1, 2, 3]
+    with pytest.raises(ValueError):
+        mu._coeff_arg([(1, 2, 3)], 2)
+    with pytest.raises(ValueError):
+        mu._coeff_arg([(1, 2)], 1)
+
+
 def test_workspace_bytes_host_logic(lib):
     def ws(shapes):
         return lib.muon_workspace_bytes(_lib.shape_array(shapes), len(shapes))
