@@ -1,4 +1,5 @@
-"""CPU oracle for the Muon optimizer step (test infrastructure only).
+"""CPU oracles for the Muon optimizer step and the multi-tensor AdamW step
+(test infrastructure only).
 
 Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
 import this package.  It shares no code with the HIP library.

@@ -1,0 +1,108 @@
+"""Plain CPU oracle of one multi-tensor AdamW step.
+
+TEST INFRASTRUCTURE ONLY.  This module is the slow, obviously-correct
+reference the HIP library's AdamW entry point is checked against.  Only the
+test suite, the smoke check and the benchmark's CPU-baseline leg may import
+it; the product path never calls it and shares no code with it.
+
+What it computes, for every parameter tensor independently (elementwise):
+the "07. Training neural networks" page (llm-generalization-bounds explainer),
+section "Adam, weight decay and AdamW" and its derivation block "Adam's bias
+correction and AdamW's decoupling, derived":
+
+    theta <- (1 - lr * lambda) * theta           decoupled weight decay, first
+    u     <- beta1 * u + (1 - beta1) * g         running mean of gradients
+    v     <- beta2 * v + (1 - beta2) * g * g     running mean of squared gradients
+    uhat  =  u / (1 - beta1^t),  vhat = v / (1 - beta2^t)     bias corrections
+    theta <- theta - lr * uhat / (sqrt(vhat) + eps)
+
+with u = v = 0 before the first step and t = 1 on the first step.  The
+thread's replies route every parameter that is not a hidden 2-D matrix to
+AdamW; the GPT-2 lecture pages apply weight decay to matrices and not to 1-D
+parameters, and fuse the AdamW update over all tensors.
+
+Readings taken where the pages are silent (each is a choice, not a quote):
+
+  W1 order            the decay multiplies theta before the Adam step, and
+                      the moments see the loss gradient alone (decoupled)
+  W2 step count       t is supplied by the caller, >= 1, one value for every
+                      tensor of a call
+  W3 precision        fp32 storage and arithmetic, one rounding per
+                      operation in the order written above, no fused
+                      multiply-add; division and square root correctly
+                      rounded.  Scalars per call: lr, beta1, beta2, eps and
+                      each lambda are fp32 values; 1 - beta1, 1 - beta2,
+                      1 - beta1^t and 1 - beta2^t are evaluated in fp64 from
+                      those fp32 values and rounded once to fp32; the decay
+                      factor is fp32(1 - fp32(lr * lambda)), per tensor
+  W4 expression form  (1 - beta2) * g * g is ((1 - beta2) * g) * g, and
+                      lr * uhat / (...) is (lr * uhat) / (...), as written
+
+Two modes:
+  "emul"   fp32 with the W3 rounding (parity with the GPU, bit for bit)
+  "exact"  fp64 everywhere (pins the algebra against the pages' printed
+           worked example and closed forms)
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+DEFAULT_BETAS = (0.9, 0.999)
+DEFAULT_EPS = 1e-8
+
+
+def step_constants(lr, beta1, beta2, eps, step):
+    """Reading W3: the per-call fp32 scalars (emul mode).  Returns a dict."""
+    f32 = np.float32
+    lr32, b1, b2, e32 = f32(lr), f32(beta1), f32(beta2), f32(eps)
+    t = int(step)
+    return {
+        "lr": lr32, "beta1": b1, "beta2": b2, "eps": e32,
+        "omb1": f32(1.0 - float(b1)), "omb2": f32(1.0 - float(b2)),
+        "bc1": f32(1.0 - float(b1) ** t), "bc2": f32(1.0 - float(b2) ** t),
+    }
+
+
+def adamw_step(p, g, u, v, lr, beta1=DEFAULT_BETAS[0], beta2=DEFAULT_BETAS[1], eps=DEFAULT_EPS,
+               weight_decay=0.0, step=1, mode="emul"):
+    """One AdamW step on one tensor.  Returns (p_new, u_new, v_new)."""
+    if int(step) < 1:
+        raise ValueError("step counts from 1")
+    if mode == "exact":
+        p = np.asarray(p, np.float64)
+        g = np.asarray(g, np.float64)
+        u = np.asarray(u, np.float64)
+        v = np.asarray(v, np.float64)
+        t = int(step)
+        p = p * (1.0 - lr * weight_decay)
+        u = beta1 * u + (1.0 - beta1) * g
+        v = beta2 * v + (1.0 - beta2) * g * g
+        uh = u / (1.0 - beta1 ** t)
+        vh = v / (1.0 - beta2 ** t)
+        p = p - lr * uh / (np.sqrt(vh) + eps)
+        return p, u, v
+    c = step_constants(lr, beta1, beta2, eps, step)
+    p = np.asarray(p, np.float32)
+    g = np.asarray(g, np.float32)
+    u = np.asarray(u, np.float32)
+    v = np.asarray(v, np.float32)
+    decay = np.float32(1.0) - (c["lr"] * np.float32(weight_decay))
+    p1 = p * decay
+    u1 = (c["beta1"] * u) + (c["omb1"] * g)
+    v1 = (c["beta2"] * v) + ((c["omb2"] * g) * g)
+    uh = u1 / c["bc1"]
+    vh = v1 / c["bc2"]
+    den = np.sqrt(vh) + c["eps"]
+    p2 = p1 - ((c["lr"] * uh) / den)
+    return p2, u1, v1
+
+
+def adamw_multi(params, grads, exp_avg, exp_avg_sq, lr, beta1=DEFAULT_BETAS[0], beta2=DEFAULT_BETAS[1],
+                eps=DEFAULT_EPS, weight_decay=0.0, step=1, mode="emul"):
+    """One step over a list of tensors; weight_decay is one value or one per
+    tensor.  Returns a list of (p, u, v)."""
+    n = len(params)
+    wds = list(weight_decay) if np.ndim(weight_decay) else [weight_decay] * n
+    return [adamw_step(params[i], grads[i], exp_avg[i], exp_avg_sq[i], lr, beta1, beta2, eps, wds[i], step, mode)
+            for i in range(n)]

@@ -58,3 +58,22 @@ def fp32(x) -> float:
 
 def bf16(x) -> float:
     return round_to(_exact(x), "bf16")
+
+
+def fp32_sqrt(x) -> float:
+    """Correctly rounded fp32 square root of a non-negative finite value
+    (ties to even), from integer square roots of the exact rational."""
+    q = _exact(x)
+    if q < 0:
+        raise ValueError("negative")
+    if q == 0:
+        return 0.0
+    p, emin, _ = _FMT["fp32"]
+    e = max(_floor_log2(q) // 2, emin)        # binade of sqrt(q)
+    quantum = Fraction(2) ** (e - p + 1)
+    k2 = q / (quantum * quantum)               # (sqrt(q) / quantum)^2
+    fl = math.isqrt(k2.numerator // k2.denominator)
+    half = (Fraction(2 * fl + 1, 2)) ** 2
+    if k2 > half or (k2 == half and fl % 2 == 1):
+        fl += 1
+    return float(fl * quantum)
