@@ -87,6 +87,46 @@ def cpu_baseline(budget_s):
                       f"{elapsed:.1f} s, scaled to the full 48-matrix step"}
 
 
+def bench_adamw(torch, mu, wl, calls=50):
+    """The multi-tensor AdamW entry on the GPT-2-124M AdamW set (the
+    parameters outside the hidden set), measured after the Muon timed region
+    and reported beside it: 28 bytes per element (read p, g, u, v; write p,
+    u, v), mean kernel time from HIP events on the launch stream."""
+    specs = wl.adamw_specs_gpt2()
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(wl.ADAMW_SEED)
+    P, G, U, V = [], [], [], []
+    for s in specs:
+        P.append(torch.randn(s.shape, generator=gen, device="cuda") * 0.02)
+        G.append(torch.randn(s.shape, generator=gen, device="cuda") * 1e-3)
+        U.append(torch.randn(s.shape, generator=gen, device="cuda") * 1e-3)
+        V.append(torch.randn(s.shape, generator=gen, device="cuda").square() * 1e-6)
+    wds = [1e-2 if s.decayed else 0.0 for s in specs]
+    n = sum(s.numel for s in specs)
+    stream = torch.cuda.current_stream()
+    for k in range(5):
+        mu.muon_adamw_step(P, G, U, V, 6e-4, (0.9, 0.999), 1e-8, wds, step=1000 + k, stream=stream)
+    torch.cuda.synchronize()
+    mu.muon_timing_enable(mu.KERNEL_ADAMW)
+    t0 = time.perf_counter()
+    for k in range(calls):
+        mu.muon_adamw_step(P, G, U, V, 6e-4, (0.9, 0.999), 1e-8, wds, step=1005 + k, stream=stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms, cnt = mu.muon_timing_read()
+    mu.muon_timing_enable(-1)
+    per = ms / max(1, cnt)
+    gbs = 28.0 * n / (per * 1e-3) / 1e9
+    del P, G, U, V
+    return {
+        "workload": "GPT-2-124M AdamW set: wte 50257x768 and wpe 1024x768 (weight decay 1e-2), 98 1-D LayerNorm "
+                    "and bias tensors (no decay); 100 fp32 tensors, 39.5M params, one launch",
+        "n_tensors": len(specs), "n_params": n, "lr": 6e-4, "betas": [0.9, 0.999], "eps": 1e-8,
+        "bytes_per_param": 28, "ms_per_launch": round(per, 5), "calls_per_s": round(calls / wall, 1),
+        "GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -96,6 +136,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-breakdown", action="store_true",
                     help="skip the per-kernel-family timing pass after the timed region")
+    ap.add_argument("--no-adamw", action="store_true", help="skip the AdamW measurement after the timed region")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -178,6 +219,8 @@ def main():
         breakdown["ns_all"] = {"ms_per_step": round(ns_ms, 5), "TFLOP/s": round(ns_tf, 1),
                                "frac_bf16_peak": round(ns_tf / PEAK_BF16_TFLOPS, 4)}
 
+    adamw = None if args.no_adamw else bench_adamw(torch, mu, wl)
+
     # A plain copy of known size, outside the timed region: it calibrates
     # rocprofv3's FETCH_SIZE / WRITE_SIZE counters when this script is profiled.
     calib = torch.empty(64 * 1024 * 1024, dtype=torch.float32, device="cuda")
@@ -225,6 +268,8 @@ def main():
     }
     if breakdown is not None:
         out["kernels"] = breakdown
+    if adamw is not None:
+        out["adamw"] = adamw
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_budget)
     print(json.dumps(out), flush=True)

@@ -124,6 +124,37 @@ int muon_newton_schulz(const uint16_t* const* x, uint16_t* const* out, const muo
 int muon_newton_schulz_sched(const uint16_t* const* x, uint16_t* const* out, const muon_shape_t* shapes,
                              int n, int ns_steps, const float* coeffs, hipStream_t stream);
 
+/*
+ * Multi-tensor AdamW step, for the parameters that are not hidden 2-D
+ * matrices (embeddings, biases, norm gains).  The update (the "07. Training
+ * neural networks" page, section "Adam, weight decay and AdamW" and its
+ * derivation of the bias correction and of the decoupled decay), for every
+ * element of tensor i, with t = step:
+ *   p <- p * (1 - lr * weight_decay[i])           decay first (decoupled)
+ *   u <- beta1 * u + (1 - beta1) * g
+ *   v <- beta2 * v + (1 - beta2) * g * g
+ *   p <- p - lr * (u / (1 - beta1^t)) / (sqrt(v / (1 - beta2^t)) + eps)
+ * fp32 throughout, one IEEE rounding per operation in the order written
+ * (no fused multiply-add; division and square root correctly rounded);
+ * 1 - beta_k and 1 - beta_k^t are evaluated in double from the fp32
+ * arguments and rounded once to fp32; the decay factor is
+ * fp32(1 - fp32(lr * weight_decay[i])).
+ *   params[i], exp_avg[i], exp_avg_sq[i]  fp32, numels[i] contiguous elements,
+ *               updated in place (exp_avg, exp_avg_sq zero before step 1)
+ *   grads[i]    fp32, numels[i] elements, read only
+ *   numels[i]   >= 0; a tensor with 0 elements is skipped (its pointers may be NULL)
+ *   weight_decay  host array of n finite values >= 0, or NULL for 0 everywhere
+ *   lr          finite;  beta1, beta2 in [0, 1);  eps finite, >= 0
+ *   step        >= 1 (t of the bias corrections: 1 on the first step)
+ * Pointers as for muon_step (device, 4-byte aligned, no two arrays
+ * overlapping).  n == 0 is a no-op; n <= MUON_ADAMW_MAX_TENSORS.  Uses no
+ * workspace; its work list is cached per pointer set like the Muon plans.
+ */
+#define MUON_ADAMW_MAX_TENSORS 65536
+int muon_adamw_step(float* const* params, const float* const* grads, float* const* exp_avg,
+                    float* const* exp_avg_sq, const int64_t* numels, const float* weight_decay, int n,
+                    float lr, float beta1, float beta2, float eps, int64_t step, hipStream_t stream);
+
 /* Thread-local description of the last failing call on this thread ("" if none). */
 const char* muon_last_error(void);
 
@@ -157,6 +188,7 @@ void muon_release(void);
 #define MUON_KERNEL_POLY 3     /* B = b A + c A A */
 #define MUON_KERNEL_UPDATE 4   /* X <- a X + B X */
 #define MUON_KERNEL_APPLY 5    /* W -= lr X */
+#define MUON_KERNEL_ADAMW 6    /* multi-tensor AdamW (muon_adamw_step) */
 int muon_timing_enable(int kernel);
 int muon_timing_read(double* total_ms, int64_t* launches);
 

@@ -13,13 +13,14 @@ import ctypes
 from . import _lib
 
 __all__ = [
-    "DEFAULT_COEFFS", "MuonError", "muon_step", "muon_newton_schulz", "muon_workspace_bytes",
+    "DEFAULT_COEFFS", "MuonError", "muon_step", "muon_newton_schulz", "muon_adamw_step", "muon_workspace_bytes",
     "muon_set_workspace", "muon_release", "muon_timing_enable", "muon_timing_read", "muon_last_error",
     "KERNEL_MOMENTUM", "KERNEL_CAST", "KERNEL_GRAM", "KERNEL_POLY", "KERNEL_UPDATE", "KERNEL_APPLY",
+    "KERNEL_ADAMW",
 ]
 
 DEFAULT_COEFFS = (3.4445, -4.7750, 2.0315)
-KERNEL_MOMENTUM, KERNEL_CAST, KERNEL_GRAM, KERNEL_POLY, KERNEL_UPDATE, KERNEL_APPLY = range(6)
+KERNEL_MOMENTUM, KERNEL_CAST, KERNEL_GRAM, KERNEL_POLY, KERNEL_UPDATE, KERNEL_APPLY, KERNEL_ADAMW = range(7)
 _CODES = {-1: "MUON_EINVAL", -2: "MUON_ENOMEM", -3: "MUON_EHIP"}
 
 
@@ -140,6 +141,46 @@ def muon_newton_schulz(xs, outs, ns_steps=5, coeffs=DEFAULT_COEFFS, stream=None)
     entry = lib.muon_newton_schulz_sched if sched else lib.muon_newton_schulz
     rc = entry(_lib.ptr_array([x.data_ptr() for x in xs]), _lib.ptr_array([o.data_ptr() for o in outs]),
                _lib.shape_array(shapes), n, int(ns_steps), C, ctypes.c_void_p(_stream_handle(stream)))
+    _check(rc)
+
+
+def _fp32_flat(t, what):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{what}: expected a tensor")
+    if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{what}: expected a contiguous float32 tensor on the GPU")
+    return t.data_ptr()
+
+
+def muon_adamw_step(params, grads, exp_avg, exp_avg_sq, lr, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.0,
+                    step=1, stream=None) -> None:
+    """One AdamW step over tensors of any shape (each contiguous fp32, taken
+    flat); exp_avg and exp_avg_sq start at zero and `step` counts from 1.
+    `weight_decay` is one value or one per tensor."""
+    n = len(params)
+    if not (len(grads) == len(exp_avg) == len(exp_avg_sq) == n):
+        raise ValueError("params, grads, exp_avg and exp_avg_sq must have the same length")
+    if hasattr(weight_decay, "__len__"):
+        wds = [float(w) for w in weight_decay]
+        if len(wds) != n:
+            raise ValueError("weight_decay: expected one value or one per tensor")
+    else:
+        wds = [float(weight_decay)] * n
+    ptrs = ([], [], [], [])
+    numels = []
+    for i in range(n):
+        ts = (params[i], grads[i], exp_avg[i], exp_avg_sq[i])
+        names = ("params", "grads", "exp_avg", "exp_avg_sq")
+        for k, (t, name) in enumerate(zip(ts, names)):
+            ptrs[k].append(_fp32_flat(t, f"{name}[{i}]"))
+        if len({t.numel() for t in ts}) != 1:
+            raise ValueError(f"tensor {i}: element counts differ")
+        numels.append(params[i].numel())
+    b1, b2 = betas
+    rc = _lib.load().muon_adamw_step(*(_lib.ptr_array(p) for p in ptrs), _lib.int64_array(numels),
+                                     _lib.float_array(wds), n, float(lr), float(b1), float(b2), float(eps),
+                                     int(step), ctypes.c_void_p(_stream_handle(stream)))
     _check(rc)
 
 

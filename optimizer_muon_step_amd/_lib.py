@@ -28,6 +28,9 @@ SIGNATURES = {
                                        ctypes.c_int, _FLOAT3, _PP, _P]),
     "muon_newton_schulz": (ctypes.c_int, [_PP, _PP, _SHAPES, ctypes.c_int, ctypes.c_int, _FLOAT3, _P]),
     "muon_newton_schulz_sched": (ctypes.c_int, [_PP, _PP, _SHAPES, ctypes.c_int, ctypes.c_int, _FLOAT3, _P]),
+    "muon_adamw_step": (ctypes.c_int, [_PP, _PP, _PP, _PP, ctypes.POINTER(ctypes.c_int64), _FLOAT3, ctypes.c_int,
+                                       ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                       ctypes.c_int64, _P]),
     "muon_last_error": (ctypes.c_char_p, []),
     "muon_workspace_bytes": (ctypes.c_size_t, [_SHAPES, ctypes.c_int]),
     "muon_set_workspace": (ctypes.c_int, [_P, ctypes.c_size_t]),
@@ -82,4 +85,11 @@ def float_array(vals):
     arr = (ctypes.c_float * max(1, len(vals)))()
     for i, v in enumerate(vals):
         arr[i] = float(v)
+    return arr
+
+
+def int64_array(vals):
+    arr = (ctypes.c_int64 * max(1, len(vals)))()
+    for i, v in enumerate(vals):
+        arr[i] = int(v)
     return arr

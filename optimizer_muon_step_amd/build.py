@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmuon.so")
-SOURCES = ["muon_api.hip", "kernels_elementwise.hip", "kernels_ns.hip"]
+SOURCES = ["muon_api.hip", "kernels_elementwise.hip", "kernels_ns.hip", "kernels_adamw.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

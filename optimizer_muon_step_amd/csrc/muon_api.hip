@@ -151,11 +151,26 @@ struct Plan {
   }
 };
 
+// AdamW work list: tensor descriptors and chunk items, cached per pointer set.
+struct AdamPlan {
+  std::vector<uintptr_t> key;
+  void* dev = nullptr;
+  void* host = nullptr;
+  AdamDesc* d_desc = nullptr;
+  EwItem* d_items = nullptr;
+  int n_items = 0;
+  ~AdamPlan() {
+    if (dev) (void)hipFree(dev);
+    if (host) (void)hipHostFree(host);
+  }
+};
+
 struct DeviceState {
   void* ws = nullptr;       // workspace in use (owned or caller's)
   size_t ws_bytes = 0;
   bool ws_owned = false;
   std::list<std::unique_ptr<Plan>> plans;  // most recent first
+  std::list<std::unique_ptr<AdamPlan>> adam_plans;  // most recent first
 };
 
 std::mutex g_mu;
@@ -519,9 +534,162 @@ int ns_entry(const uint16_t* const* x, uint16_t* const* out, const muon_shape_t*
   return run(MODE_NS, nullptr, nullptr, nullptr, out, x, shapes, n, 0.0f, 0.0f, ns_steps, coeffs, stride, stream);
 }
 
+// ---------------------------------------------------------------- AdamW ----
+
+int get_adam_plan(DeviceState& st, int n, float* const* params, const float* const* grads, float* const* u,
+                  float* const* v, const int64_t* numels, const float* wd, hipStream_t stream, AdamPlan** out) {
+  std::vector<uintptr_t> key;
+  key.reserve(1 + 6 * (size_t)n);
+  key.push_back((uintptr_t)n);
+  for (int i = 0; i < n; ++i) {
+    uint32_t wbits = 0;
+    const float w = wd ? wd[i] : 0.0f;
+    memcpy(&wbits, &w, sizeof wbits);
+    key.push_back((uintptr_t)params[i]);
+    key.push_back((uintptr_t)grads[i]);
+    key.push_back((uintptr_t)u[i]);
+    key.push_back((uintptr_t)v[i]);
+    key.push_back((uintptr_t)numels[i]);
+    key.push_back((uintptr_t)wbits);
+  }
+  for (auto it = st.adam_plans.begin(); it != st.adam_plans.end(); ++it) {
+    if ((*it)->key == key) {
+      if (it != st.adam_plans.begin()) st.adam_plans.splice(st.adam_plans.begin(), st.adam_plans, it);
+      *out = st.adam_plans.front().get();
+      return MUON_OK;
+    }
+  }
+  auto plan = std::make_unique<AdamPlan>();
+  plan->key = std::move(key);
+  std::vector<AdamDesc> desc(n);
+  std::vector<EwItem> items;
+  for (int i = 0; i < n; ++i) {
+    AdamDesc& d = desc[i];
+    memset(&d, 0, sizeof d);
+    d.p = params[i];
+    d.g = grads[i];
+    d.u = u[i];
+    d.v = v[i];
+    d.numel = numels[i];
+    d.wd = wd ? wd[i] : 0.0f;
+    d.vec4 = ((uintptr_t)d.p % 16 == 0) && ((uintptr_t)d.g % 16 == 0) && ((uintptr_t)d.u % 16 == 0) &&
+             ((uintptr_t)d.v % 16 == 0);
+    const int64_t chunks = (numels[i] + ADAM_CHUNK - 1) / ADAM_CHUNK;
+    for (int64_t c = 0; c < chunks; ++c) items.push_back({i, (int32_t)c});
+  }
+  if (items.size() > (size_t)INT32_MAX) return fail(MUON_EINVAL, "AdamW call of %zu chunks is too large", items.size());
+  const size_t o_desc = 0;
+  const size_t o_items = align_up(sizeof(AdamDesc) * n);
+  const size_t bytes = std::max<size_t>(o_items + align_up(sizeof(EwItem) * items.size()), kAlign);
+  hipError_t e;
+  if ((e = hipHostMalloc(&plan->host, bytes, hipHostMallocDefault)) != hipSuccess) {
+    plan->host = nullptr;
+    return fail(MUON_ENOMEM, "hipHostMalloc of %zu plan bytes failed: %s", bytes, hipGetErrorString(e));
+  }
+  if ((e = hipMalloc(&plan->dev, bytes)) != hipSuccess) {
+    plan->dev = nullptr;
+    (void)hipGetLastError();
+    return fail(MUON_ENOMEM, "hipMalloc of %zu plan bytes failed: %s", bytes, hipGetErrorString(e));
+  }
+  char* h = static_cast<char*>(plan->host);
+  memcpy(h + o_desc, desc.data(), sizeof(AdamDesc) * n);
+  memcpy(h + o_items, items.data(), sizeof(EwItem) * items.size());
+  if ((e = hipMemcpyAsync(plan->dev, plan->host, bytes, hipMemcpyHostToDevice, stream)) != hipSuccess)
+    return fail_hip(e, "hipMemcpyAsync(adamw plan)");
+  if ((e = hipStreamSynchronize(stream)) != hipSuccess) return fail_hip(e, "hipStreamSynchronize(adamw plan)");
+  plan->d_desc = reinterpret_cast<AdamDesc*>(static_cast<char*>(plan->dev) + o_desc);
+  plan->d_items = reinterpret_cast<EwItem*>(static_cast<char*>(plan->dev) + o_items);
+  plan->n_items = (int)items.size();
+  st.adam_plans.push_front(std::move(plan));
+  while (st.adam_plans.size() > kMaxPlans) st.adam_plans.pop_back();
+  *out = st.adam_plans.front().get();
+  return MUON_OK;
+}
+
+int validate_adamw(float* const* params, const float* const* grads, float* const* u, float* const* v,
+                   const int64_t* numels, const float* wd, int n, float lr, float beta1, float beta2, float eps,
+                   int64_t step) {
+  if (n < 0 || n > MUON_ADAMW_MAX_TENSORS)
+    return fail(MUON_EINVAL, "n = %d outside [0, %d]", n, MUON_ADAMW_MAX_TENSORS);
+  if (n > 0 && (!params || !grads || !u || !v || !numels))
+    return fail(MUON_EINVAL, "params, grads, exp_avg, exp_avg_sq and numels arrays must not be NULL");
+  if (!std::isfinite(lr)) return fail(MUON_EINVAL, "lr is not finite");
+  if (!std::isfinite(beta1) || beta1 < 0.0f || beta1 >= 1.0f) return fail(MUON_EINVAL, "beta1 = %g outside [0, 1)", (double)beta1);
+  if (!std::isfinite(beta2) || beta2 < 0.0f || beta2 >= 1.0f) return fail(MUON_EINVAL, "beta2 = %g outside [0, 1)", (double)beta2);
+  if (!std::isfinite(eps) || eps < 0.0f) return fail(MUON_EINVAL, "eps = %g is not finite and >= 0", (double)eps);
+  if (step < 1) return fail(MUON_EINVAL, "step = %lld: the first step is 1", (long long)step);
+  std::vector<Range> r;
+  r.reserve(4 * (size_t)n);
+  for (int i = 0; i < n; ++i) {
+    if (numels[i] < 0) return fail(MUON_EINVAL, "numels[%d] = %lld is negative", i, (long long)numels[i]);
+    if (wd && (!std::isfinite(wd[i]) || wd[i] < 0.0f))
+      return fail(MUON_EINVAL, "weight_decay[%d] = %g is not finite and >= 0", i, (double)wd[i]);
+    if (numels[i] == 0) continue;
+    if (numels[i] > (int64_t)1 << 40) return fail(MUON_EINVAL, "numels[%d] = %lld is too large", i, (long long)numels[i]);
+    const size_t fb = (size_t)numels[i] * sizeof(float);
+    const void* ptrs[4] = {params[i], grads[i], u[i], v[i]};
+    const char* names[4] = {"params", "grads", "exp_avg", "exp_avg_sq"};
+    for (int k = 0; k < 4; ++k) {
+      if (!ptrs[k]) return fail(MUON_EINVAL, "%s[%d] is NULL", names[k], i);
+      if ((uintptr_t)ptrs[k] % 4) return fail(MUON_EINVAL, "%s[%d] is not 4-byte aligned", names[k], i);
+      r.push_back({(uintptr_t)ptrs[k], (uintptr_t)ptrs[k] + fb, i, names[k]});
+    }
+  }
+  return check_ranges(r);
+}
+
+int adamw_entry(float* const* params, const float* const* grads, float* const* u, float* const* v,
+                const int64_t* numels, const float* wd, int n, float lr, float beta1, float beta2, float eps,
+                int64_t step, hipStream_t stream) {
+  g_error.clear();
+  int rc = validate_adamw(params, grads, u, v, numels, wd, n, lr, beta1, beta2, eps, step);
+  if (rc) return rc;
+  // tensors with elements; empty ones are dropped before planning
+  std::vector<float*> P, U, V;
+  std::vector<const float*> G;
+  std::vector<int64_t> N;
+  std::vector<float> W;
+  for (int i = 0; i < n; ++i) {
+    if (numels[i] == 0) continue;
+    P.push_back(params[i]);
+    G.push_back(grads[i]);
+    U.push_back(u[i]);
+    V.push_back(v[i]);
+    N.push_back(numels[i]);
+    W.push_back(wd ? wd[i] : 0.0f);
+  }
+  if (P.empty()) return MUON_OK;
+  AdamConst c{};
+  c.lr = lr;
+  c.beta1 = beta1;
+  c.beta2 = beta2;
+  c.eps = eps;
+  c.omb1 = (float)(1.0 - (double)beta1);
+  c.omb2 = (float)(1.0 - (double)beta2);
+  c.bc1 = (float)(1.0 - std::pow((double)beta1, (double)step));
+  c.bc2 = (float)(1.0 - std::pow((double)beta2, (double)step));
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceState& st = g_dev[dev];
+  AdamPlan* p = nullptr;
+  if ((rc = get_adam_plan(st, (int)P.size(), P.data(), G.data(), U.data(), V.data(), N.data(), W.data(), stream, &p)))
+    return rc;
+  return timed(MUON_KERNEL_ADAMW, stream, [&] { return launch_adamw(p->d_desc, p->d_items, p->n_items, c, stream); },
+               "adamw kernel launch");
+}
+
 }  // namespace
 
 extern "C" {
+
+int muon_adamw_step(float* const* params, const float* const* grads, float* const* exp_avg,
+                    float* const* exp_avg_sq, const int64_t* numels, const float* weight_decay, int n,
+                    float lr, float beta1, float beta2, float eps, int64_t step, hipStream_t stream) {
+  return adamw_entry(params, grads, exp_avg, exp_avg_sq, numels, weight_decay, n, lr, beta1, beta2, eps, step,
+                     stream);
+}
 
 int muon_step_ex(float* const* params, const float* const* grads, float* const* momentum,
                  const muon_shape_t* shapes, int n, float lr, float beta, int ns_steps, const float* coeffs,
@@ -590,6 +758,7 @@ void muon_release(void) {
     if (hipSetDevice(kv.first) != hipSuccess) continue;
     (void)hipDeviceSynchronize();
     kv.second.plans.clear();
+    kv.second.adam_plans.clear();
     if (kv.second.ws && kv.second.ws_owned) (void)hipFree(kv.second.ws);
   }
   (void)hipSetDevice(cur);
@@ -601,7 +770,7 @@ void muon_release(void) {
 
 int muon_timing_enable(int kernel) {
   g_error.clear();
-  if (kernel < -1 || kernel > MUON_KERNEL_APPLY) return fail(MUON_EINVAL, "unknown kernel family %d", kernel);
+  if (kernel < -1 || kernel > MUON_KERNEL_ADAMW) return fail(MUON_EINVAL, "unknown kernel family %d", kernel);
   std::lock_guard<std::mutex> lock(g_mu);
   g_time_kind = kernel;
   g_ev_used = 0;

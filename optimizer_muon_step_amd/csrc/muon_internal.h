@@ -63,6 +63,28 @@ struct EwItem {
 
 enum GemmKind { GEMM_GRAM = 0, GEMM_POLY = 1, GEMM_UPDATE = 2 };
 
+// ---- multi-tensor AdamW ----
+constexpr int ADAM_CHUNK = 4096;  // elements per work item (4 float4 per thread per array)
+
+// One tensor of an AdamW call (flat, contiguous fp32).
+struct AdamDesc {
+  float* p;        // parameters, updated in place
+  const float* g;  // gradient
+  float* u;        // first moment (exp_avg), updated in place
+  float* v;        // second moment (exp_avg_sq), updated in place
+  int64_t numel;
+  float wd;        // this tensor's weight decay lambda
+  int32_t vec4;    // 1 when all four arrays are 16-byte aligned
+};
+
+// Per-call scalars: the fp32 arguments and the constants derived from them
+// on the host (fp64, rounded once to fp32).
+struct AdamConst {
+  float lr, beta1, beta2, eps;
+  float omb1, omb2;  // 1 - beta1, 1 - beta2
+  float bc1, bc2;    // 1 - beta1^t, 1 - beta2^t
+};
+
 // ---- host launchers (kernels_*.hip) ----
 hipError_t launch_momentum(const MatDesc* d, const EwItem* items, int n_items, int n_mats, float beta,
                            hipStream_t s);
@@ -72,5 +94,6 @@ hipError_t launch_apply(const MatDesc* d, const EwItem* items, int n_items, floa
                         int write_w, hipStream_t s);
 hipError_t launch_gemm(int kind, const MatDesc* d, const GemmItem* items, int n_items, int src,
                        float ca, float cb, float cc, hipStream_t s);
+hipError_t launch_adamw(const AdamDesc* d, const EwItem* items, int n_items, const AdamConst& c, hipStream_t s);
 
 }  // namespace muon

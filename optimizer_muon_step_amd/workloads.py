@@ -27,6 +27,17 @@ and the XL width 1600 / 48 layers are the standard GPT-2 family shapes):
       plus a 768x768 matrix with singular values log-spaced from 1e-6 to 1
 
 Initial parameters are N(0, 0.02^2) (GPT-2's init std); momentum starts at 0.
+
+AdamW workload (the GPT-2-124M parameters outside the hidden set, which the
+thread's replies route to AdamW): the token embedding 50257x768 (tied with
+the output layer) and the position embedding 1024x768, weight-decayed; per
+layer the two LayerNorm gains and biases (768 each) and the four linear
+biases (2304, 768, 3072, 768), and the final LayerNorm's gain and bias, all
+1-D and not decayed (the GPT-2 lecture pages decay matrices, not 1-D
+parameters).  100 tensors, 39,505,152 elements.  Parameters N(0, 0.02^2),
+gradients N(0, 1e-3^2) per tensor scaled by 10^U, U ~ U(-1, 1); for a
+mid-training step the moments are drawn too (exp_avg N(0, 1e-3^2), exp_avg_sq
+the square of another such draw).
 """
 
 from __future__ import annotations
@@ -145,3 +156,50 @@ def make_matrix(name: str, idx: int, steps: int = 1) -> dict:
 
 def n_params(name: str) -> int:
     return sum(s.rows * s.cols for s in config_specs(name))
+
+
+# ------------------------------------------------------------------ AdamW --
+
+ADAMW_SEED = 2000
+
+
+@dataclass(frozen=True)
+class TensorSpec:
+    name: str
+    shape: tuple
+    decayed: bool
+
+    @property
+    def numel(self) -> int:
+        n = 1
+        for d in self.shape:
+            n *= d
+        return n
+
+
+def adamw_specs_gpt2() -> list[TensorSpec]:
+    w = GPT2_WIDTH
+    specs = [TensorSpec("wte", (VOCAB, w), True), TensorSpec("wpe", (1024, w), True)]
+    for layer in range(GPT2_LAYERS):
+        for nm, n in (("ln_1.weight", w), ("ln_1.bias", w), ("attn.c_attn.bias", 3 * w), ("attn.c_proj.bias", w),
+                      ("ln_2.weight", w), ("ln_2.bias", w), ("mlp.c_fc.bias", 4 * w), ("mlp.c_proj.bias", w)):
+            specs.append(TensorSpec(f"h.{layer}.{nm}", (n,), False))
+    specs += [TensorSpec("ln_f.weight", (w,), False), TensorSpec("ln_f.bias", (w,), False)]
+    return specs
+
+
+def make_adamw_tensor(idx: int, spec: TensorSpec, step: int = 1, moments: bool = False) -> dict:
+    """Inputs for one AdamW tensor: params, a gradient for `step`, and the
+    moments (zero, or drawn when `moments`)."""
+    rng = _rng(ADAMW_SEED, idx, 0)
+    p = rng.standard_normal(spec.shape, dtype=np.float32) * np.float32(0.02)
+    scale = 1e-3 * 10.0 ** _rng(ADAMW_SEED, idx, 1 << 20).uniform(-1.0, 1.0)
+    g = _rng(ADAMW_SEED, idx, step).standard_normal(spec.shape, dtype=np.float32) * np.float32(scale)
+    if moments:
+        mr = _rng(ADAMW_SEED, idx, 1 << 21)
+        u = mr.standard_normal(spec.shape, dtype=np.float32) * np.float32(1e-3)
+        v = np.square(mr.standard_normal(spec.shape, dtype=np.float32) * np.float32(1e-3))
+    else:
+        u = np.zeros(spec.shape, np.float32)
+        v = np.zeros(spec.shape, np.float32)
+    return {"spec": spec, "p": p, "g": g, "u": u, "v": v}

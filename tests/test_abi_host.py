@@ -124,6 +124,36 @@ def test_schedule_entries_validate_every_triple(lib):
     assert rc == -1 and "coeffs" in lib.muon_last_error().decode()
 
 
+def test_adamw_validation_before_any_hip_call(lib):
+    P = [_lib.ptr_array([0x10000 * (k + 1)]) for k in range(4)]
+    n1 = _lib.int64_array([64])
+
+    def call(ptrs=P, numels=n1, wd=None, n=1, lr=1e-3, b1=0.9, b2=0.999, eps=1e-8, step=1):
+        return lib.muon_adamw_step(*ptrs, numels, wd, n, lr, b1, b2, eps, step, None)
+
+    cases = [
+        (dict(step=0), "step"),
+        (dict(b1=1.0), "beta1"),
+        (dict(b2=-0.1), "beta2"),
+        (dict(eps=-1e-8), "eps"),
+        (dict(eps=float("nan")), "eps"),
+        (dict(lr=float("inf")), "lr"),
+        (dict(wd=_lib.float_array([-0.1])), "weight_decay[0]"),
+        (dict(numels=_lib.int64_array([-1])), "numels[0]"),
+        (dict(n=-1), "n = -1"),
+        (dict(ptrs=[P[0], P[1], P[2], _lib.ptr_array([0])]), "exp_avg_sq[0] is NULL"),
+        (dict(ptrs=[P[0], P[1], P[2], _lib.ptr_array([0x10002])]), "4-byte aligned"),
+        (dict(ptrs=[P[0], P[1], P[2], _lib.ptr_array([0x10000 + 128])]), "overlaps"),
+    ]
+    for kw, msg in cases:
+        assert call(**kw) == -1, kw
+        assert msg in lib.muon_last_error().decode(), (kw, lib.muon_last_error())
+    # no tensors, or only empty ones (whose pointers may be NULL): nothing to do, no device needed
+    assert call(n=0) == 0
+    nul = _lib.ptr_array([0])
+    assert call(ptrs=[nul] * 4, numels=_lib.int64_array([0])) == 0
+
+
 def test_binding_coefficient_forms():
     import optimizer_muon_step_amd as mu
     sched, arr = mu._coeff_arg([(1, 2, 3), (4, 5, 6)], 2)
