@@ -155,6 +155,22 @@ int muon_adamw_step(float* const* params, const float* const* grads, float* cons
                     float* const* exp_avg_sq, const int64_t* numels, const float* weight_decay, int n,
                     float lr, float beta1, float beta2, float eps, int64_t step, hipStream_t stream);
 
+/*
+ * Delayed untying of a shared parameter (the "nanoGPT Speedrun Techniques:
+ * How Delayed Untying Solves the Sparse Gradient Problem" page, section
+ * "Option B: Delayed Untying"): the parameter and both of its AdamW moments
+ * (rows x cols fp32 each, row-major) are copied into new buffers, so that the
+ * new parameter's trajectory continues from the shared point instead of
+ * restarting its moments.  transpose = 1 writes the copies as cols x rows
+ * (an output layer stored d_model x vocab against a vocab x d_model
+ * embedding); transpose = 0 copies as is.  rows, cols >= 1 with
+ * rows * cols <= 2^40; all six pointers device, 4-byte aligned, no
+ * destination overlapping another array.  Bit-exact copies.
+ */
+int muon_adamw_untie(const float* param, const float* exp_avg, const float* exp_avg_sq, float* new_param,
+                     float* new_exp_avg, float* new_exp_avg_sq, int64_t rows, int64_t cols, int transpose,
+                     hipStream_t stream);
+
 /* Thread-local description of the last failing call on this thread ("" if none). */
 const char* muon_last_error(void);
 

@@ -13,7 +13,8 @@ import ctypes
 from . import _lib
 
 __all__ = [
-    "DEFAULT_COEFFS", "MuonError", "muon_step", "muon_newton_schulz", "muon_adamw_step", "muon_workspace_bytes",
+    "DEFAULT_COEFFS", "MuonError", "matrix_shape", "muon_step", "muon_newton_schulz", "muon_adamw_step", "muon_adamw_untie",
+    "muon_workspace_bytes",
     "muon_set_workspace", "muon_release", "muon_timing_enable", "muon_timing_read", "muon_last_error",
     "KERNEL_MOMENTUM", "KERNEL_CAST", "KERNEL_GRAM", "KERNEL_POLY", "KERNEL_UPDATE", "KERNEL_APPLY",
     "KERNEL_ADAMW",
@@ -48,10 +49,24 @@ def _stream_handle(stream):
     return stream.cuda_stream
 
 
+def matrix_shape(shape):
+    """The matrix a parameter of rank >= 2 is orthogonalised as: its first
+    dimension by the product of the others (for a convolution filter
+    out x in x kh x kw, the out x (in kh kw) matrix of its im2col form).  A
+    contiguous row-major tensor already is that matrix in memory."""
+    shape = tuple(int(d) for d in shape)
+    if len(shape) < 2:
+        raise ValueError("rank >= 2 expected (1-D parameters belong to another optimizer)")
+    cols = 1
+    for d in shape[1:]:
+        cols *= d
+    return shape[0], cols
+
+
 def _fp32_matrix(t, what):
     import torch
-    if not isinstance(t, torch.Tensor) or t.dim() != 2:
-        raise ValueError(f"{what}: expected a 2-D tensor (1-D parameters belong to another optimizer)")
+    if not isinstance(t, torch.Tensor) or t.dim() < 2:
+        raise ValueError(f"{what}: expected a tensor of rank >= 2 (1-D parameters belong to another optimizer)")
     if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
         raise ValueError(f"{what}: expected a contiguous float32 tensor on the GPU")
     return t.data_ptr()
@@ -59,8 +74,8 @@ def _fp32_matrix(t, what):
 
 def _bf16_matrix(t, what):
     import torch
-    if not isinstance(t, torch.Tensor) or t.dim() != 2:
-        raise ValueError(f"{what}: expected a 2-D tensor")
+    if not isinstance(t, torch.Tensor) or t.dim() < 2:
+        raise ValueError(f"{what}: expected a tensor of rank >= 2")
     if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16) or not t.is_cuda or not t.is_contiguous():
         raise ValueError(f"{what}: expected a contiguous bfloat16 tensor on the GPU")
     return t.data_ptr()
@@ -82,9 +97,11 @@ def _coeff_arg(coeffs, ns_steps):
 
 def muon_step(params, grads, momentum, lr=0.02, beta=0.95, ns_steps=5, coeffs=DEFAULT_COEFFS,
               updates=None, stream=None) -> None:
-    """One Muon step over lists of 2-D fp32 tensors (params and momentum updated in place).
+    """One Muon step over lists of fp32 tensors of rank >= 2 (params and
+    momentum updated in place; rank > 2 is taken as the matrix_shape view).
     `coeffs` is one (a, b, c) or a schedule of ns_steps triples.  `updates`, if
-    given, is a list of bf16 tensors (or None entries) receiving the applied update."""
+    given, is a list of bf16 tensors (or None entries) of the params' shapes
+    receiving the applied update."""
     n = len(params)
     if len(grads) != n or len(momentum) != n:
         raise ValueError("params, grads and momentum must have the same length")
@@ -93,7 +110,7 @@ def muon_step(params, grads, momentum, lr=0.02, beta=0.95, ns_steps=5, coeffs=DE
         _fp32_matrix(p, f"params[{i}]"), _fp32_matrix(g, f"grads[{i}]"), _fp32_matrix(m, f"momentum[{i}]")
         if g.shape != p.shape or m.shape != p.shape:
             raise ValueError(f"matrix {i}: shapes differ")
-        shapes.append(tuple(p.shape))
+        shapes.append(matrix_shape(p.shape))
     lib = _lib.load()
     P = _lib.ptr_array([p.data_ptr() for p in params])
     G = _lib.ptr_array([g.data_ptr() for g in grads])
@@ -115,7 +132,7 @@ def muon_step(params, grads, momentum, lr=0.02, beta=0.95, ns_steps=5, coeffs=DE
                 ptrs.append(None)
                 continue
             _bf16_matrix(u, f"updates[{i}]")
-            if tuple(u.shape) != shapes[i]:
+            if u.shape != params[i].shape:
                 raise ValueError(f"updates[{i}]: shape differs from params[{i}]")
             ptrs.append(u.data_ptr())
         U = _lib.ptr_array(ptrs)
@@ -135,7 +152,7 @@ def muon_newton_schulz(xs, outs, ns_steps=5, coeffs=DEFAULT_COEFFS, stream=None)
         _bf16_matrix(x, f"xs[{i}]"), _bf16_matrix(o, f"outs[{i}]")
         if x.shape != o.shape:
             raise ValueError(f"matrix {i}: shapes differ")
-        shapes.append(tuple(x.shape))
+        shapes.append(matrix_shape(x.shape))
     lib = _lib.load()
     sched, C = _coeff_arg(coeffs, ns_steps)
     entry = lib.muon_newton_schulz_sched if sched else lib.muon_newton_schulz
@@ -182,6 +199,26 @@ def muon_adamw_step(params, grads, exp_avg, exp_avg_sq, lr, betas=(0.9, 0.999), 
                                      _lib.float_array(wds), n, float(lr), float(b1), float(b2), float(eps),
                                      int(step), ctypes.c_void_p(_stream_handle(stream)))
     _check(rc)
+
+
+def muon_adamw_untie(param, exp_avg, exp_avg_sq, transpose=False, stream=None):
+    """Delayed untying: new (param, exp_avg, exp_avg_sq) tensors copied from
+    a shared 2-D parameter and its AdamW moments, transposed if asked, so the
+    untied parameter continues from the shared point.  Returns the three new
+    tensors (allocated here, filled by the library on the stream)."""
+    import torch
+    for t, name in ((param, "param"), (exp_avg, "exp_avg"), (exp_avg_sq, "exp_avg_sq")):
+        _fp32_flat(t, name)
+        if t.dim() != 2 or t.shape != param.shape:
+            raise ValueError(f"{name}: expected a 2-D tensor of the parameter's shape")
+    rows, cols = param.shape
+    shape = (cols, rows) if transpose else (rows, cols)
+    out = [torch.empty(shape, dtype=torch.float32, device=param.device) for _ in range(3)]
+    rc = _lib.load().muon_adamw_untie(param.data_ptr(), exp_avg.data_ptr(), exp_avg_sq.data_ptr(),
+                                      out[0].data_ptr(), out[1].data_ptr(), out[2].data_ptr(), rows, cols,
+                                      1 if transpose else 0, ctypes.c_void_p(_stream_handle(stream)))
+    _check(rc)
+    return tuple(out)
 
 
 def muon_workspace_bytes(shapes) -> int:

@@ -31,6 +31,7 @@ SIGNATURES = {
     "muon_adamw_step": (ctypes.c_int, [_PP, _PP, _PP, _PP, ctypes.POINTER(ctypes.c_int64), _FLOAT3, ctypes.c_int,
                                        ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_float,
                                        ctypes.c_int64, _P]),
+    "muon_adamw_untie": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, _P]),
     "muon_last_error": (ctypes.c_char_p, []),
     "muon_workspace_bytes": (ctypes.c_size_t, [_SHAPES, ctypes.c_int]),
     "muon_set_workspace": (ctypes.c_int, [_P, ctypes.c_size_t]),

@@ -18,6 +18,9 @@
 // reuse, so they are loaded and stored non-temporally.  A full chunk of a
 // tensor whose four arrays are 16-byte aligned moves as float4, all loads of
 // the chunk issued before any arithmetic; other chunks go element by element.
+//
+// Also here: the transposed copy of a parameter and its moments used when a
+// tied embedding / output layer pair is untied.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -96,6 +99,42 @@ __global__ __launch_bounds__(EW_THREADS) void adamw_kernel(const AdamDesc* __res
       Q[e] = ve;
     }
   }
+}
+
+// Delayed untying: copy a shared parameter and its two AdamW moments into
+// new buffers, transposed (rows x cols -> cols x rows).  One 64x64 tile per
+// block and array; rows are read and written as whole 256-byte segments, the
+// transpose happens in LDS (row stride 65 words, so the column reads of the
+// write-out hit 64 different banks).
+constexpr int UNTIE_TILE = 64;
+
+__global__ __launch_bounds__(EW_THREADS) void untie_transpose_kernel(UntieArgs a, int64_t rows, int64_t cols,
+                                                                     int64_t tiles_c) {
+  __shared__ float tile[UNTIE_TILE][UNTIE_TILE + 1];
+  const int64_t tr = blockIdx.x / tiles_c, tc = blockIdx.x % tiles_c;
+  const int64_t r0 = tr * UNTIE_TILE, c0 = tc * UNTIE_TILE;
+  const int lx = threadIdx.x % UNTIE_TILE, ly = threadIdx.x / UNTIE_TILE;  // 64 x 4 threads
+  for (int k = 0; k < 3; ++k) {
+    const MUON_GLOBAL float* src = gptr(a.src[k]);
+    MUON_GLOBAL float* dst = gptr(a.dst[k]);
+    for (int y = ly; y < UNTIE_TILE; y += EW_THREADS / UNTIE_TILE) {
+      const int64_t r = r0 + y, c = c0 + lx;
+      if (r < rows && c < cols) tile[y][lx] = src[r * cols + c];
+    }
+    __syncthreads();
+    for (int y = ly; y < UNTIE_TILE; y += EW_THREADS / UNTIE_TILE) {
+      const int64_t r = c0 + y, c = r0 + lx;  // destination row = source column
+      if (r < cols && c < rows) dst[r * rows + c] = tile[lx][y];
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_untie_transpose(const UntieArgs& a, int64_t rows, int64_t cols, hipStream_t s) {
+  const int64_t tiles_r = (rows + UNTIE_TILE - 1) / UNTIE_TILE, tiles_c = (cols + UNTIE_TILE - 1) / UNTIE_TILE;
+  if (tiles_r * tiles_c == 0) return hipSuccess;
+  untie_transpose_kernel<<<(unsigned)(tiles_r * tiles_c), EW_THREADS, 0, s>>>(a, rows, cols, tiles_c);
+  return hipGetLastError();
 }
 
 hipError_t launch_adamw(const AdamDesc* d, const EwItem* items, int n_items, const AdamConst& c, hipStream_t s) {

@@ -680,9 +680,55 @@ int adamw_entry(float* const* params, const float* const* grads, float* const* u
                "adamw kernel launch");
 }
 
+int untie_entry(const float* const src[3], float* const dst[3], int64_t rows, int64_t cols, int transpose,
+                hipStream_t stream) {
+  g_error.clear();
+  if (rows < 1 || cols < 1) return fail(MUON_EINVAL, "rows = %lld, cols = %lld: both must be >= 1", (long long)rows, (long long)cols);
+  if (rows > ((int64_t)1 << 40) / cols) return fail(MUON_EINVAL, "rows * cols above 2^40");
+  if (transpose != 0 && transpose != 1) return fail(MUON_EINVAL, "transpose = %d is neither 0 nor 1", transpose);
+  const char* sn[3] = {"param", "exp_avg", "exp_avg_sq"};
+  const char* dn[3] = {"new_param", "new_exp_avg", "new_exp_avg_sq"};
+  const size_t b = (size_t)rows * cols * sizeof(float);
+  std::vector<Range> r;
+  for (int k = 0; k < 3; ++k) {
+    if (!src[k] || !dst[k]) return fail(MUON_EINVAL, "%s or %s is NULL", sn[k], dn[k]);
+    if ((uintptr_t)src[k] % 4 || (uintptr_t)dst[k] % 4) return fail(MUON_EINVAL, "%s or %s is not 4-byte aligned", sn[k], dn[k]);
+    r.push_back({(uintptr_t)dst[k], (uintptr_t)dst[k] + b, 0, dn[k]});
+  }
+  int rc = check_ranges(r);
+  if (rc) return rc;
+  // sources may share memory with one another (read only), never with a destination
+  for (int k = 0; k < 3; ++k)
+    for (int j = 0; j < 3; ++j)
+      if ((uintptr_t)src[k] < (uintptr_t)dst[j] + b && (uintptr_t)dst[j] < (uintptr_t)src[k] + b)
+        return fail(MUON_EINVAL, "%s overlaps %s", sn[k], dn[j]);
+  hipError_t e;
+  if (!transpose) {
+    for (int k = 0; k < 3; ++k)
+      if ((e = hipMemcpyAsync(dst[k], src[k], b, hipMemcpyDeviceToDevice, stream)) != hipSuccess)
+        return fail_hip(e, "hipMemcpyAsync(untie)");
+    return MUON_OK;
+  }
+  UntieArgs a{};
+  for (int k = 0; k < 3; ++k) {
+    a.src[k] = src[k];
+    a.dst[k] = dst[k];
+  }
+  if ((e = launch_untie_transpose(a, rows, cols, stream)) != hipSuccess) return fail_hip(e, "untie kernel launch");
+  return MUON_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int muon_adamw_untie(const float* param, const float* exp_avg, const float* exp_avg_sq, float* new_param,
+                     float* new_exp_avg, float* new_exp_avg_sq, int64_t rows, int64_t cols, int transpose,
+                     hipStream_t stream) {
+  const float* src[3] = {param, exp_avg, exp_avg_sq};
+  float* dst[3] = {new_param, new_exp_avg, new_exp_avg_sq};
+  return untie_entry(src, dst, rows, cols, transpose, stream);
+}
 
 int muon_adamw_step(float* const* params, const float* const* grads, float* const* exp_avg,
                     float* const* exp_avg_sq, const int64_t* numels, const float* weight_decay, int n,

@@ -96,4 +96,12 @@ hipError_t launch_gemm(int kind, const MatDesc* d, const GemmItem* items, int n_
                        float ca, float cb, float cc, hipStream_t s);
 hipError_t launch_adamw(const AdamDesc* d, const EwItem* items, int n_items, const AdamConst& c, hipStream_t s);
 
+// Source and destination of the three arrays (param, exp_avg, exp_avg_sq)
+// of a delayed-untying copy.
+struct UntieArgs {
+  const float* src[3];
+  float* dst[3];
+};
+hipError_t launch_untie_transpose(const UntieArgs& a, int64_t rows, int64_t cols, hipStream_t s);
+
 }  // namespace muon

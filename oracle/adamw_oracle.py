@@ -106,3 +106,15 @@ def adamw_multi(params, grads, exp_avg, exp_avg_sq, lr, beta1=DEFAULT_BETAS[0], 
     wds = list(weight_decay) if np.ndim(weight_decay) else [weight_decay] * n
     return [adamw_step(params[i], grads[i], exp_avg[i], exp_avg_sq[i], lr, beta1, beta2, eps, wds[i], step, mode)
             for i in range(n)]
+
+
+def untie_state(p, u, v, transpose=False):
+    """Delayed untying (the "nanoGPT Speedrun Techniques: How Delayed Untying
+    Solves the Sparse Gradient Problem" page, section "Option B: Delayed
+    Untying"): the new parameter starts as a copy of the shared one together
+    with both AdamW moments, so that its trajectory continues from the shared
+    point.  With `transpose` the copies are laid out as the transpose (the
+    output layer stored d_model x vocab, the page's description of lm_head
+    against the vocab x d_model embedding)."""
+    f = (lambda a: np.ascontiguousarray(np.asarray(a).T)) if transpose else (lambda a: np.array(a, copy=True))
+    return f(p), f(u), f(v)

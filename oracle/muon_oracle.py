@@ -42,6 +42,11 @@ Readings taken where the pages are silent (each one is a choice, not a quote):
   R7 apply                W <- W - lr * O with no extra scale and no weight
                           decay (the thread's replies report weight decay as
                           worse), rounded once per operation in fp32
+  R10 rank > 2            a parameter of shape (d0, d1, ..., dk) is the matrix
+                          d0 x (d1 ... dk), its trailing dimensions flattened
+                          in row-major order: the im2col view of a
+                          convolution filter that a reply to the thread
+                          suggests for tensors of any shape
 
 Two modes:
   "emul"  fp32 arithmetic with bf16 rounding at the R5 storage points (parity)
@@ -189,6 +194,18 @@ def muon_step_matrix(W, g, buf, lr, beta, ns_steps, coeffs=DEFAULT_COEFFS, mode=
     O, X0, s = orthogonalize(u, ns_steps, coeffs, mode)
     W_new = apply_update(W, O, lr, mode)
     return {"W": W_new, "buf": buf_new, "O": O, "X0": X0, "s": s, "u": u}
+
+
+def muon_step_tensor(W, g, buf, lr, beta, ns_steps, coeffs=DEFAULT_COEFFS, mode="emul"):
+    """Reading R10: one Muon step on a parameter of rank >= 2, taken as the
+    matrix (first dimension) x (product of the others).  Results come back in
+    the tensor's shape."""
+    shape = np.shape(W)
+    if len(shape) < 2:
+        raise ValueError("rank >= 2 expected")
+    m = (shape[0], int(np.prod(shape[1:])))
+    r = muon_step_matrix(np.reshape(W, m), np.reshape(g, m), np.reshape(buf, m), lr, beta, ns_steps, coeffs, mode)
+    return {k: (np.reshape(v, shape) if k in ("W", "buf", "O", "u") else v) for k, v in r.items()}
 
 
 def muon_step(params, grads, moms, lr, beta, ns_steps, coeffs=DEFAULT_COEFFS, mode="emul"):

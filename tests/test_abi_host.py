@@ -154,6 +154,36 @@ def test_adamw_validation_before_any_hip_call(lib):
     assert call(ptrs=[nul] * 4, numels=_lib.int64_array([0])) == 0
 
 
+def test_untie_validation_before_any_hip_call(lib):
+    src = [0x100000, 0x200000, 0x300000]
+    dst = [0x400000, 0x500000, 0x600000]
+
+    def call(s=src, d=dst, rows=64, cols=32, tr=1):
+        return lib.muon_adamw_untie(*s, *d, rows, cols, tr, None)
+
+    cases = [
+        (dict(rows=0), "rows = 0"),
+        (dict(cols=-3), "cols = -3"),
+        (dict(rows=1 << 30, cols=1 << 20), "2^40"),
+        (dict(tr=2), "transpose = 2"),
+        (dict(s=[0, src[1], src[2]]), "NULL"),
+        (dict(d=[dst[0], dst[1] + 2, dst[2]]), "4-byte aligned"),
+        (dict(d=[dst[0], dst[0] + 1024, dst[2]]), "overlaps"),
+        (dict(s=[src[0], dst[2] - 512, src[2]]), "exp_avg overlaps new_exp_avg_sq"),
+    ]
+    for kw, msg in cases:
+        assert call(**kw) == -1, kw
+        assert msg in lib.muon_last_error().decode(), (kw, lib.muon_last_error())
+
+
+def test_matrix_shape_of_higher_rank():
+    import optimizer_muon_step_amd as mu
+    assert mu.matrix_shape((64, 32, 3, 3)) == (64, 288)
+    assert mu.matrix_shape((5, 7)) == (5, 7)
+    with pytest.raises(ValueError):
+        mu.matrix_shape((9,))
+
+
 def test_binding_coefficient_forms():
     import optimizer_muon_step_amd as mu
     sched, arr = mu._coeff_arg([(1, 2, 3), (4, 5, 6)], 2)

@@ -269,3 +269,32 @@ def test_mutations_are_caught(monkeypatch):
                 failed += 1
         assert failed >= 1, bad.__name__
     monkeypatch.undo()
+
+
+@pytest.mark.parametrize("transpose", [False, True])
+def test_untied_copy_continues_the_shared_trajectory(transpose):
+    """The page's point: copying the weights and both moments lets the
+    untied parameter continue exactly where the shared one was (its next
+    step with the same gradient equals the shared tensor's next step, bit
+    for bit, up to the layout), while restarting the moments from zero does
+    not (the bias correction restarts and the momentum is lost)."""
+    rng = np.random.default_rng(70)
+    shape = (37, 11)
+    p = rng.standard_normal(shape).astype(np.float32)
+    u = (rng.standard_normal(shape) * 1e-2).astype(np.float32)
+    v = (rng.random(shape) * 1e-3).astype(np.float32)
+    g = rng.standard_normal(shape).astype(np.float32)
+    t = 500
+    shared = ao.adamw_step(p, g, u, v, 1e-3, 0.9, 0.999, 1e-8, 0.0, t)
+    cp, cu, cv = ao.untie_state(p, u, v, transpose)
+    assert cp.shape == (shape[::-1] if transpose else shape)
+    gl = np.ascontiguousarray(g.T) if transpose else g
+    untied = ao.adamw_step(cp, gl, cu, cv, 1e-3, 0.9, 0.999, 1e-8, 0.0, t)
+    for a, b in zip(shared, untied):
+        b = b.T if transpose else b
+        assert np.array_equal(a.view(np.uint32), np.ascontiguousarray(b).view(np.uint32))
+    z = np.zeros_like(cu)
+    reset = ao.adamw_step(cp, gl, z, z, 1e-3, 0.9, 0.999, 1e-8, 0.0, t)
+    assert not np.allclose(reset[0], untied[0], rtol=0, atol=1e-5)
+    # the copies are independent buffers
+    assert not any(np.shares_memory(a, b) for a, b in zip((cp, cu, cv), (p, u, v)))

@@ -143,7 +143,8 @@ def test_adamw_special_values():
         P, G, U, V = to_gpu(p0), to_gpu(g), to_gpu(z), to_gpu(z)
         mu.muon_adamw_step([P], [G], [U], [V], 1e-2, (0.9, 0.999), eps, 0.1, step=1)
         torch.cuda.synchronize()
-        p, u, v = ao.adamw_step(p0, g, z, z, 1e-2, 0.9, 0.999, eps, 0.1, 1)
+        with np.errstate(over="ignore", divide="ignore", invalid="ignore"):
+            p, u, v = ao.adamw_step(p0, g, z, z, 1e-2, 0.9, 0.999, eps, 0.1, 1)
         for got, want, tag in ((P, p, "p"), (U, u, "u"), (V, v, "v")):
             got = got.cpu().numpy()
             assert np.array_equal(np.isnan(got), np.isnan(want)), tag
@@ -195,3 +196,31 @@ def test_adamw_empty_tensors_and_timing():
     assert launches == 1 and ms > 0
     p, _, _ = ao.adamw_step(p0, g, np.zeros(5000, np.float32), np.zeros(5000, np.float32), 1e-3)
     _bits_equal(P.cpu().numpy(), p, "p")
+
+
+@pytest.mark.parametrize("shape,transpose", [((50257, 768), True), ((70, 130), True), ((1, 5), True),
+                                             ((300, 7), False)])
+def test_untie_copies_param_and_moments(shape, transpose):
+    torch = torch_mod()
+    import optimizer_muon_step_amd as mu
+    rng = np.random.default_rng(shape[0] + shape[1])
+    host = [rng.standard_normal(shape).astype(np.float32) for _ in range(3)]
+    host[2] = np.abs(host[2])
+    dev = [to_gpu(h) for h in host]
+    say(f"[untie] {shape} transpose={transpose}")
+    out = mu.muon_adamw_untie(*dev, transpose=transpose)
+    torch.cuda.synchronize()
+    want = ao.untie_state(*host, transpose)
+    for o, w, tag in zip(out, want, ("param", "exp_avg", "exp_avg_sq")):
+        assert tuple(o.shape) == w.shape
+        _bits_equal(o.cpu().numpy(), w, tag)
+    # the untied copy continues the shared trajectory (one AdamW step each)
+    g = rng.standard_normal(shape).astype(np.float32)
+    gd = to_gpu(g)
+    gt = to_gpu(np.ascontiguousarray(g.T)) if transpose else to_gpu(g)
+    mu.muon_adamw_step([dev[0]], [gd], [dev[1]], [dev[2]], 1e-3, step=50)
+    mu.muon_adamw_step([out[0]], [gt], [out[1]], [out[2]], 1e-3, step=50)
+    torch.cuda.synchronize()
+    for a, b in zip(dev, out):
+        b = b.t() if transpose else b
+        assert torch.equal(a, b.contiguous())

@@ -278,3 +278,26 @@ def test_caller_workspace():
                        "grads": [np.ones((512, 512), np.float32)]}], "grads", 1)
     finally:
         mu.muon_set_workspace(None, 0)
+
+
+@pytest.mark.parametrize("shape", [(64, 32, 3, 3), (300, 4, 5), (8, 3, 5, 5)])
+def test_rank_above_two_is_the_flattened_matrix(shape):
+    """A filter (out, in, kh, kw) is stepped as the out x (in kh kw) matrix:
+    bit-identical to passing that 2-D view, and within the bar of the oracle."""
+    torch = torch_mod()
+    import optimizer_muon_step_amd as mu
+    rng = np.random.default_rng(sum(shape))
+    W0 = (rng.standard_normal(shape) * 0.02).astype(np.float32)
+    g = rng.standard_normal(shape).astype(np.float32)
+    Wt, Gt, Mt = to_gpu(W0), to_gpu(g), torch.zeros(shape, device="cuda")
+    Ut = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    mu.muon_step([Wt], [Gt], [Mt], LR, BETA, 5, COEFFS, updates=[Ut])
+    m = mu.matrix_shape(shape)
+    W2, G2, M2 = to_gpu(W0.reshape(m)), to_gpu(g.reshape(m)), torch.zeros(m, device="cuda")
+    mu.muon_step([W2], [G2], [M2], LR, BETA, 5, COEFFS)
+    torch.cuda.synchronize()
+    assert torch.equal(Wt.reshape(m), W2) and torch.equal(Mt.reshape(m), M2)
+    r = om.muon_step_tensor(W0, g, np.zeros_like(g), LR, BETA, 5, COEFFS)
+    e = rel_f(bf16_to_np(Ut), r["O"])
+    say(f"  {shape} as {m}: update relF {e:.2e}")
+    assert bf16_to_np(Ut).shape == shape and e <= NS_TOL

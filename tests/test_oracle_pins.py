@@ -526,3 +526,51 @@ def test_textbook_quintic_schedule_reaches_the_polar_factor():
 def test_schedule_shape_is_checked():
     with pytest.raises(ValueError):
         om.newton_schulz(np.zeros((4, 6), np.float32), 3, [COEFFS] * 2)
+
+
+# ------------------------------------------------------------ rank > 2 --
+
+def test_rank_four_filter_is_its_im2col_matrix():
+    """Reading R10: a conv filter (out, in, kh, kw) is orthogonalised as the
+    matrix whose row o holds, in order over (in, y, x), the filter taps; that
+    matrix is built here tap by tap, and the exact-mode result must be its
+    SVD closed form, folded back the same way."""
+    rng = np.random.default_rng(60)
+    o, i, kh, kw = 6, 4, 3, 3
+    g = rng.standard_normal((o, i, kh, kw))
+    M = np.zeros((o, i * kh * kw))
+    for a in range(o):
+        col = 0
+        for b in range(i):
+            for y in range(kh):
+                for x in range(kw):
+                    M[a, col] = g[a, b, y, x]
+                    col += 1
+    r = om.muon_step_tensor(np.zeros_like(g), g, np.zeros_like(g), 1.0, 0.0, 5, COEFFS, mode="exact")
+    U, sig, Vt = np.linalg.svd(M / (np.linalg.norm(M) + om.NORM_EPS), full_matrices=False)
+    want = (U * p_scalar(sig, 5)) @ Vt
+    got = np.zeros_like(want)
+    for a in range(o):
+        col = 0
+        for b in range(i):
+            for y in range(kh):
+                for x in range(kw):
+                    got[a, col] = r["O"][a, b, y, x]
+                    col += 1
+    assert r["O"].shape == g.shape
+    assert rel_f(got, want) < 1e-8
+    # W <- W - lr O in the tensor's own shape
+    assert np.allclose(r["W"], -r["O"], atol=0)
+
+
+def test_rank_three_tall_tensor_is_transposed_like_a_tall_matrix():
+    """(12, 2, 3) is the 12 x 6 matrix: more rows than columns, so it is
+    iterated transposed; emul mode must equal the 2-D call bit for bit."""
+    rng = np.random.default_rng(61)
+    g = rng.standard_normal((12, 2, 3)).astype(np.float32)
+    W = rng.standard_normal((12, 2, 3)).astype(np.float32)
+    r3 = om.muon_step_tensor(W, g, np.zeros_like(g), 0.02, 0.95, 5)
+    r2 = om.muon_step_matrix(W.reshape(12, 6), g.reshape(12, 6), np.zeros((12, 6), np.float32), 0.02, 0.95, 5)
+    assert np.array_equal(r3["O"].reshape(12, 6), r2["O"]) and np.array_equal(r3["W"].reshape(12, 6), r2["W"])
+    with pytest.raises(ValueError):
+        om.muon_step_tensor(W[0, 0], g[0, 0], g[0, 0], 0.02, 0.95, 5)
