@@ -337,25 +337,28 @@ int get_plan(DeviceState& st, int mode, int n, const muon_shape_t* shapes, float
   // GEMM tiles.  Per matrix in an order that reuses operands (update: all row
   // tiles of one column block in a row, sharing that block of X; symmetric
   // phases: upper-triangle tiles row by row), then spread over the XCDs.
-  std::vector<GemmItem> gram_seq, upd_seq;
+  // Gram and poly tiles differ in size (256 and 128).
+  std::vector<GemmItem> gram_seq, poly_seq, upd_seq;
   std::vector<int64_t> gram_cost, upd_cost;
   for (int i = 0; i < n; ++i) {
-    const int tm = desc[i].m_pad / SYM_BM, tn = desc[i].n_pad / UPD_BN;
-    for (int ti = 0; ti < tm; ++ti)
-      for (int tj = ti; tj < tm; ++tj) {
+    const int tg = desc[i].m_pad / GRAM_BM, tm = desc[i].m_pad / SYM_BM, tn = desc[i].n_pad / UPD_BN;
+    for (int ti = 0; ti < tg; ++ti)
+      for (int tj = ti; tj < tg; ++tj) {
         gram_seq.push_back({i, (int16_t)ti, (int16_t)tj});
         gram_cost.push_back(desc[i].n_pad);
       }
+    for (int ti = 0; ti < tm; ++ti)
+      for (int tj = ti; tj < tm; ++tj) poly_seq.push_back({i, (int16_t)ti, (int16_t)tj});
     for (int tj = 0; tj < tn; ++tj)
       for (int ti = 0; ti < desc[i].m_pad / UPD_ROWU; ti += UPD_BM / UPD_ROWU) {
         upd_seq.push_back({i, (int16_t)ti, (int16_t)tj});
         upd_cost.push_back(desc[i].m_pad);
       }
   }
-  std::vector<int64_t> poly_cost(gram_seq.size());
-  for (size_t k = 0; k < gram_seq.size(); ++k) poly_cost[k] = desc[gram_seq[k].mat].m_pad;
+  std::vector<int64_t> poly_cost(poly_seq.size());
+  for (size_t k = 0; k < poly_seq.size(); ++k) poly_cost[k] = desc[poly_seq[k].mat].m_pad;
   gram = xcd_interleave(gram_seq, gram_cost);
-  poly = xcd_interleave(gram_seq, poly_cost);
+  poly = xcd_interleave(poly_seq, poly_cost);
   updl = xcd_interleave(upd_seq, upd_cost);
 
   size_t off = 0;

@@ -9,11 +9,12 @@ namespace muon {
 // Tile geometry of the Newton-Schulz GEMMs.  Inside the workspace the
 // canonical m is padded to NS_PAD_M and n to NS_PAD_N, with the padding held
 // at exact zero, so the GEMM kernels never bounds-check.
-constexpr int SYM_BM = 128, SYM_BN = 128;  // GRAM / POLY output tile
+constexpr int GRAM_BM = 256;               // GRAM output tile (square), 8 waves
+constexpr int SYM_BM = 128, SYM_BN = 128;  // POLY output tile
 constexpr int SYM_BK = 64, SYM_NSTAGE = 2;  // GRAM / POLY K slice and ring depth (measured best)
 constexpr int UPD_BM = 192, UPD_BN = 256;  // UPDATE output tile (rows may overhang m_pad)
 constexpr int UPD_ROWU = 64;               // UPDATE tile rows start at multiples of this
-constexpr int NS_PAD_M = 128;              // multiple of SYM_BM and SYM_BN
+constexpr int NS_PAD_M = 256;              // multiple of GRAM_BM and SYM_BM
 constexpr int NS_PAD_N = 256;              // multiple of UPD_BN
 constexpr int NS_THREADS = 256;
 // Row strides of X (n_pad + NS_LD_PAD) and of A / B (m_pad + NS_LD_PAD), in
