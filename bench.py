@@ -168,6 +168,15 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # The library creates its timing events on first use and reuses them after
+    # each read: one untimed pass with timing on fills the pool, so that no
+    # event is created inside the timed region.
+    mu.muon_timing_enable(mu.KERNEL_UPDATE)
+    for _ in range(args.steps):
+        step()
+    mu.muon_timing_read()
+    mu.muon_timing_enable(-1)
+    torch.cuda.synchronize()
 
     # Timed region: K steps; the update GEMM's launches are bracketed by HIP
     # events on this stream.

@@ -24,7 +24,7 @@ constexpr int NS_LD_PAD = 64;
 
 // Elementwise kernels.
 constexpr int EW_THREADS = 256;
-constexpr int MOM_CHUNK = 8192;   // elements per momentum work item (8 float4 per thread)
+constexpr int MOM_CHUNK = 16384;  // elements per momentum work item (16 float4 per thread and array)
 constexpr int CAST_TILE = 64;     // square tile for the cast / apply kernels
 
 // One matrix of a call, in device memory.

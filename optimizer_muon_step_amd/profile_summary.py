@@ -39,6 +39,8 @@ FAMILIES = [
     (r"norm_finalize_kernel", "norm_finalize"),
     (r"cast_kernel", "cast"),
     (r"apply_kernel", "apply"),
+    (r"adamw_kernel", "adamw"),
+    (r"untie_transpose_kernel", "untie"),
     (r"copyBuffer", "copy"),
 ]
 
@@ -77,6 +79,18 @@ def cmd_trace(args):
         lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                      f"{100 * float(r['TotalDurationNs']) / total:.1f}% |")
+    for w in args.window or []:
+        fam, first, count = w.split(":")
+        first, count = int(first), int(count)
+        trace = [r for r in csv.DictReader(open(os.path.join(args.dir, "run_kernel_trace.csv")))
+                 if family(r["Kernel_Name"]) == fam]
+        trace.sort(key=lambda r: int(r["Dispatch_Id"]))
+        sel = trace[first:first + count]
+        if len(sel) != count:
+            raise SystemExit(f"window {w}: only {len(sel)} launches")
+        mean = sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in sel) / count / 1e3
+        lines += ["", f"{fam} launches {first + 1}-{first + count} (in dispatch order; the benchmark's timed "
+                      f"region): mean {mean:.2f} us over {count} launches."]
     open(args.out, "w").write("\n".join(lines) + "\n")
 
 
@@ -145,6 +159,8 @@ def main():
     t.add_argument("--command", required=True)
     t.add_argument("--title", default="Kernel trace summary")
     t.add_argument("--note", default="")
+    t.add_argument("--window", action="append",
+                   help="FAMILY:FIRST:COUNT, mean duration of that family's launches FIRST..FIRST+COUNT-1")
     r = sub.add_parser("traffic")
     r.add_argument("fetch_dir")
     r.add_argument("write_dir")
