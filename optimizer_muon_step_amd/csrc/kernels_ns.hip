@@ -533,7 +533,7 @@ hipError_t launch_gemm(int kind, const MatDesc* d, const GemmItem* items, int n_
       ns_gemm_kernel<GEMM_GRAM, GRAM_BM, GRAM_BM, 2, 4, 2, GRAM_BM, 64><<<n_items, 512, 0, s>>>(d, items, src, ca, cb, cc);
       break;
     case GEMM_POLY:
-      ns_gemm_kernel<GEMM_POLY, SYM_BM, SYM_BN, 2, 2, SYM_NSTAGE, SYM_BM, SYM_BK><<<n_items, 256, 0, s>>>(d, items, src, ca, cb, cc);
+      ns_gemm_kernel<GEMM_POLY, SYM_BM, SYM_BN, 2, 4, SYM_NSTAGE, SYM_BM, SYM_BK><<<n_items, 512, 0, s>>>(d, items, src, ca, cb, cc);
       break;
     default:
       ns_gemm_kernel<GEMM_UPDATE, UPD_BM, UPD_BN, 2, 4, 2, UPD_ROWU, 64><<<n_items, 512, 0, s>>>(d, items, src, ca, cb, cc);
