@@ -131,19 +131,15 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const M
   constexpr int RB = BK * 2;        // bytes per k-contiguous row of a slice
   constexpr int CPR = BK / 8;       // 16-byte chunks per k-contiguous row
   constexpr int RPI = 1024 / RB;    // k-contiguous rows per wave DMA instruction
-  // UPDATE: K slices holding the tile's own rows, and the ones kept past the
-  // two stage buffers so that all of them are in LDS when the loop ends.
-  constexpr int OWN = NN ? BM / BK : 0;
-  constexpr int EXTRA = (OWN > 2) ? OWN - 2 : 0;
   static_assert(A_INSTR >= 1 && B_INSTR >= 1 && A_INSTR * 16 * NT == A_BYTES && B_INSTR * 16 * NT == B_BYTES,
                 "tile does not split into whole DMA instructions");
   static_assert(NSTAGE >= 2 && NSTAGE <= 4 && TM >= 1 && TN >= 1, "unsupported tile");
   static_assert(!NN || BK == 64, "the k-major X slice is read 64 rows at a time");
-  static_assert(!NN || ((TN == 2 || TN == 4) && BM % BK == 0 && OWN <= 3 && ROWU == BK && (NSTAGE == 2 || OWN <= 2)),
-                "UPDATE tiling: tile rows a whole number (<= 3) of K slices, kept in the ring or aside");
+  static_assert(!NN || ((TN == 2 || TN == 4) && BM % 32 == 0 && BK % 32 == 0 && ROWU % 32 == 0),
+                "UPDATE tiling: 32-row blocks of the tile each inside one K slice");
   static_assert(NN || ROWU == BM, "symmetric tiles are addressed in units of their own size");
   static_assert(!NN || BN >= 128, "k-major swizzle needs 16 chunks per row");
-  __shared__ __attribute__((aligned(16))) char lds[NSTAGE * STAGE_BYTES + EXTRA * B_BYTES];
+  __shared__ __attribute__((aligned(16))) char lds[NSTAGE * STAGE_BYTES];
 
   const GemmItem it = items[blockIdx.x];
   if (it.mat < 0) return;  // padding item of a shorter per-XCD run
@@ -167,17 +163,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const M
   const int col0 = it.tj * BN;  // output columns: rows of Bop (GRAM/POLY), columns of X (UPDATE)
   const int row_lim = d.m_pad;
   const int KT = K / BK;
-
-  // K order.  UPDATE visits the slices holding its own rows last, so that
-  // when the loop ends they are still in LDS (the last two stage buffers,
-  // plus one slice copied aside) for the a*X term of the epilogue.  The order
-  // of the fp32 sum is the only thing that changes.
-  int n_own = 0, kt0 = 0;
-  if (NN) {
-    n_own = min(OWN, KT - row0 / BK);
-    kt0 = (row0 / BK + n_own) % KT;
-  }
-  auto kt_of = [&](int s) { int k = kt0 + s; return k >= KT ? k - KT : k; };
+  // K is walked in order, slice s = k-range s*BK .. s*BK+BK-1, by every tile:
+  // the row tiles of one UPDATE column block fetch the same X slices at about
+  // the same time and share them in L2.
+  auto kt_of = [&](int s) { return s; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -337,10 +326,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const M
   };
 
   // Epilogue inputs come out of staged K slices that already hold them, so
-  // they cost no extra global traffic.  POLY: A[i][j] is column k = j of the
-  // A slice, picked up during the loop.  UPDATE: X[i][j] is row k = i of the
-  // k-major X slice, read after the loop from the slices kept in LDS.  The
-  // epilogue combines them in the fixed order of the storage-point reading.
+  // they cost no extra global traffic; both are picked up during the loop.
+  // POLY: A[i][j] is column k = j of the A slice.  UPDATE: X[i][j] is row
+  // k = i of the k-major X slice.  The epilogue combines them in the fixed
+  // order of the storage-point reading.
   u32x2 ein[TM][TN][4];
 #pragma unroll
   for (int mi = 0; mi < TM; ++mi)
@@ -365,17 +354,24 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const M
         }
     }
   };
-  LDS_AS char* const extra = (LDS_AS char*)lds + NSTAGE * STAGE_BYTES;
-  // UPDATE: an own slice that is not among the last two is copied aside
-  // (16-byte chunks, all threads) before its stage buffer is refilled.
-  auto keep_slice = [&](int s) {
-    const int slot = s - (KT - n_own);
-    if (slot < 0 || slot >= n_own - 2) return;
-    const LDS_AS char* from = (const LDS_AS char*)lds + (s % NSTAGE) * STAGE_BYTES + A_BYTES;
-    LDS_AS char* to = extra + slot * B_BYTES;
+  auto capture_update = [&](int s) {
+    // slice s holds X rows s*BK .. s*BK+BK-1; a 32-row block of output rows
+    // lies inside one slice (rows past m_pad fall in none and are not stored)
+    const LDS_AS char* slice = (const LDS_AS char*)lds + (s % NSTAGE) * STAGE_BYTES + A_BYTES;
+    const int kt = kt_of(s);
 #pragma unroll
-    for (int c = 0; c < B_BYTES / (16 * NT); ++c)
-      *(LDS_AS u32x4*)(to + (c * NT + tid) * 16) = *(const LDS_AS u32x4*)(from + (c * NT + tid) * 16);
+    for (int mi = 0; mi < TM; ++mi) {
+      const int grow = row0 + wi * WTM + mi * 32;
+      if (grow / BK != kt) continue;
+      const int lr = grow % BK + (lane & 31);
+#pragma unroll
+      for (int nj = 0; nj < TN; ++nj)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const int cl = wj * WTN + nj * 32 + 8 * e4 + 4 * (lane >> 5);
+          ein[mi][nj][e4] = *(const LDS_AS u32x2*)(slice + lr * (BN * 2) + swz_n(lr, cl >> 3) * 16 + (cl & 7) * 2);
+        }
+    }
   };
 
   // Main loop over s = 0 .. KT-1 (slice kt_of(s), stage buffer s % NSTAGE).
@@ -401,7 +397,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const M
     asm volatile("" ::: "memory");
     if (s + NSTAGE - 1 < KT) issue(s + NSTAGE - 1);
     if constexpr (KIND == GEMM_POLY) capture_poly(s);
-    if constexpr (EXTRA > 0) keep_slice(s);
+    if constexpr (NN) capture_update(s);
     compute(s);
   }
 
@@ -413,29 +409,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const M
   wait_vm_lgkm0<0>();
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-  if constexpr (NN) {
-    // own slice j (rows j*BK .. of the tile) was step KT - n_own + j
-#pragma unroll
-    for (int mi = 0; mi < TM; ++mi) {
-      const int tr = wi * WTM + mi * 32;  // tile row of this 32-row block
-      const int j = tr / BK;
-      if (j >= n_own) continue;  // rows past m_pad: never stored
-      const int step = KT - n_own + j;
-      const LDS_AS char* slice = (step >= KT - 2) ? (const LDS_AS char*)lds + (step % NSTAGE) * STAGE_BYTES + A_BYTES
-                                                  : (const LDS_AS char*)extra + j * B_BYTES;
-      const int lr = tr % BK + (lane & 31);
-#pragma unroll
-      for (int nj = 0; nj < TN; ++nj)
-#pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-          const int cl = wj * WTN + nj * 32 + 8 * e4 + 4 * (lane >> 5);
-          ein[mi][nj][e4] = *(const LDS_AS u32x2*)(slice + lr * (BN * 2) + swz_n(lr, cl >> 3) * 16 + (cl & 7) * 2);
-        }
-    }
-    wait_vm_lgkm0<0>();
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-  }
   LDS_AS char* E = (LDS_AS char*)lds;
   constexpr int ROWB = BN * 2;          // staged row bytes
   constexpr int RCH = BN / 8;           // 16-byte chunks per staged row
