@@ -149,6 +149,11 @@ int muon_newton_schulz_sched(const uint16_t* const* x, uint16_t* const* out, con
  * Pointers as for muon_step (device, 4-byte aligned, no two arrays
  * overlapping).  n == 0 is a no-op; n <= MUON_ADAMW_MAX_TENSORS.  Uses no
  * workspace; its work list is cached per pointer set like the Muon plans.
+ * lr, the betas, eps and step are launch arguments, and so is the first
+ * non-zero weight_decay value, shared by every tensor that uses it: a
+ * schedule of those values reuses the cached list.  Only a tensor whose
+ * non-zero lambda differs from that shared value has its lambda cached with
+ * the list.
  */
 #define MUON_ADAMW_MAX_TENSORS 65536
 int muon_adamw_step(float* const* params, const float* const* grads, float* const* exp_avg,

@@ -56,7 +56,7 @@ __global__ __launch_bounds__(EW_THREADS) void adamw_kernel(const AdamDesc* __res
   const AdamDesc& d = descs[it.mat];
   const int64_t base = (int64_t)it.idx * ADAM_CHUNK;
   const int64_t end = min(base + (int64_t)ADAM_CHUNK, d.numel);
-  const float decay = 1.0f - c.lr * d.wd;
+  const float decay = 1.0f - c.lr * (d.wd_shared ? c.wd_shared : d.wd);
   MUON_GLOBAL float* P = gptr(d.p);
   const MUON_GLOBAL float* G = gptr(d.g);
   MUON_GLOBAL float* U = gptr(d.u);

@@ -539,21 +539,26 @@ int ns_entry(const uint16_t* const* x, uint16_t* const* out, const muon_shape_t*
 
 // ---------------------------------------------------------------- AdamW ----
 
+// wd[i] is a tensor's own lambda, baked into the plan, unless shared[i] is
+// set: then the call's shared lambda (a kernel argument) applies.  The shared
+// lambda can change from call to call (a weight-decay schedule) without a new
+// plan.
 int get_adam_plan(DeviceState& st, int n, float* const* params, const float* const* grads, float* const* u,
-                  float* const* v, const int64_t* numels, const float* wd, hipStream_t stream, AdamPlan** out) {
+                  float* const* v, const int64_t* numels, const float* wd, const int* shared, hipStream_t stream,
+                  AdamPlan** out) {
   std::vector<uintptr_t> key;
-  key.reserve(1 + 6 * (size_t)n);
+  key.reserve(1 + 7 * (size_t)n);
   key.push_back((uintptr_t)n);
   for (int i = 0; i < n; ++i) {
     uint32_t wbits = 0;
-    const float w = wd ? wd[i] : 0.0f;
-    memcpy(&wbits, &w, sizeof wbits);
+    memcpy(&wbits, &wd[i], sizeof wbits);
     key.push_back((uintptr_t)params[i]);
     key.push_back((uintptr_t)grads[i]);
     key.push_back((uintptr_t)u[i]);
     key.push_back((uintptr_t)v[i]);
     key.push_back((uintptr_t)numels[i]);
-    key.push_back((uintptr_t)wbits);
+    key.push_back((uintptr_t)shared[i]);
+    key.push_back(shared[i] ? 0 : (uintptr_t)wbits);
   }
   for (auto it = st.adam_plans.begin(); it != st.adam_plans.end(); ++it) {
     if ((*it)->key == key) {
@@ -574,7 +579,8 @@ int get_adam_plan(DeviceState& st, int n, float* const* params, const float* con
     d.u = u[i];
     d.v = v[i];
     d.numel = numels[i];
-    d.wd = wd ? wd[i] : 0.0f;
+    d.wd = shared[i] ? 0.0f : wd[i];
+    d.wd_shared = shared[i];
     d.vec4 = ((uintptr_t)d.p % 16 == 0) && ((uintptr_t)d.g % 16 == 0) && ((uintptr_t)d.u % 16 == 0) &&
              ((uintptr_t)d.v % 16 == 0);
     const int64_t chunks = (numels[i] + ADAM_CHUNK - 1) / ADAM_CHUNK;
@@ -662,7 +668,18 @@ int adamw_entry(float* const* params, const float* const* grads, float* const* u
     W.push_back(wd ? wd[i] : 0.0f);
   }
   if (P.empty()) return MUON_OK;
+  // The first non-zero lambda is the call's shared one; every tensor that
+  // uses it takes it from the kernel arguments.
+  std::vector<int> S(W.size(), 0);
+  float shared_wd = 0.0f;
+  for (float w : W)
+    if (w != 0.0f) {
+      shared_wd = w;
+      break;
+    }
+  for (size_t i = 0; i < W.size(); ++i) S[i] = (W[i] != 0.0f && W[i] == shared_wd) ? 1 : 0;
   AdamConst c{};
+  c.wd_shared = shared_wd;
   c.lr = lr;
   c.beta1 = beta1;
   c.beta2 = beta2;
@@ -677,7 +694,8 @@ int adamw_entry(float* const* params, const float* const* grads, float* const* u
   std::lock_guard<std::mutex> lock(g_mu);
   DeviceState& st = g_dev[dev];
   AdamPlan* p = nullptr;
-  if ((rc = get_adam_plan(st, (int)P.size(), P.data(), G.data(), U.data(), V.data(), N.data(), W.data(), stream, &p)))
+  if ((rc = get_adam_plan(st, (int)P.size(), P.data(), G.data(), U.data(), V.data(), N.data(), W.data(), S.data(), stream,
+                          &p)))
     return rc;
   return timed(MUON_KERNEL_ADAMW, stream, [&] { return launch_adamw(p->d_desc, p->d_items, p->n_items, c, stream); },
                "adamw kernel launch");

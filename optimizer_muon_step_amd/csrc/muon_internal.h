@@ -74,8 +74,10 @@ struct AdamDesc {
   float* u;        // first moment (exp_avg), updated in place
   float* v;        // second moment (exp_avg_sq), updated in place
   int64_t numel;
-  float wd;        // this tensor's weight decay lambda
-  int32_t vec4;    // 1 when all four arrays are 16-byte aligned
+  float wd;           // this tensor's weight decay lambda (when not shared)
+  int32_t wd_shared;  // 1: the call's shared lambda (AdamConst::wd_shared) applies
+  int32_t vec4;       // 1 when all four arrays are 16-byte aligned
+  int32_t pad_;
 };
 
 // Per-call scalars: the fp32 arguments and the constants derived from them
@@ -84,6 +86,7 @@ struct AdamConst {
   float lr, beta1, beta2, eps;
   float omb1, omb2;  // 1 - beta1, 1 - beta2
   float bc1, bc2;    // 1 - beta1^t, 1 - beta2^t
+  float wd_shared;   // the lambda of every tensor flagged wd_shared
 };
 
 // ---- host launchers (kernels_*.hip) ----

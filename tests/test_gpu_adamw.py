@@ -224,3 +224,30 @@ def test_untie_copies_param_and_moments(shape, transpose):
     for a, b in zip(dev, out):
         b = b.t() if transpose else b
         assert torch.equal(a, b.contiguous())
+
+
+def test_adamw_weight_decay_schedule_bit_exact():
+    """lambda changing every step (a schedule), a tensor with a lambda of its
+    own, tensors without decay, and a step where every lambda is zero."""
+    rng = np.random.default_rng(35)
+    sizes = [5000, 300, 4096, 777]
+    schedule = [[0.1, 0.0, 0.1, 0.3], [0.05, 0.0, 0.05, 0.3], [0.2, 0.0, 0.2, 0.2], [0.0, 0.0, 0.0, 0.0],
+                [0.1, 0.0, 0.1, 0.3]]
+    ts = [{"p": rng.standard_normal(n).astype(np.float32),
+           "g": [rng.standard_normal(n).astype(np.float32) for _ in schedule],
+           "u": np.zeros(n, np.float32), "v": np.zeros(n, np.float32)} for n in sizes]
+    torch = torch_mod()
+    import optimizer_muon_step_amd as mu
+    P = [to_gpu(t["p"]) for t in ts]
+    U = [to_gpu(t["u"]) for t in ts]
+    V = [to_gpu(t["v"]) for t in ts]
+    want = [(t["p"], t["u"], t["v"]) for t in ts]
+    for s, wds in enumerate(schedule):
+        mu.muon_adamw_step(P, [to_gpu(t["g"][s]) for t in ts], U, V, 1e-2, (0.9, 0.999), 1e-8, wds, step=s + 1)
+        want = [ao.adamw_step(*want[i][:1], ts[i]["g"][s], *want[i][1:], 1e-2, 0.9, 0.999, 1e-8, wds[i], s + 1)
+                for i in range(len(ts))]
+    torch.cuda.synchronize()
+    for i, (wp, wu, wv) in enumerate(want):
+        _bits_equal(P[i].cpu().numpy(), wp, f"p[{i}]")
+        _bits_equal(U[i].cpu().numpy(), wu, f"u[{i}]")
+        _bits_equal(V[i].cpu().numpy(), wv, f"v[{i}]")
