@@ -127,6 +127,44 @@ def bench_adamw(torch, mu, wl, calls=50):
     }
 
 
+def bench_small(torch, mu, wl, steps=200):
+    """Small workloads, where launch overhead matters: steps/s of eager calls
+    and of the same step captured once into a HIP graph and replayed."""
+    out = {}
+    for name in ("c1", "c2"):
+        specs = wl.config_specs(name)
+        W = [torch.from_numpy(wl.make_params(name, i, s)).cuda() for i, s in enumerate(specs)]
+        G = [torch.from_numpy(wl.make_grad(name, i, s, 1)).cuda() for i, s in enumerate(specs)]
+        M = [torch.zeros((s.rows, s.cols), device="cuda") for s in specs]
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(10):
+                mu.muon_step(W, G, M, LR, BETA, NS_STEPS, COEFFS)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                mu.muon_step(W, G, M, LR, BETA, NS_STEPS, COEFFS)
+            torch.cuda.synchronize()
+            eager = steps / (time.perf_counter() - t0)
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            mu.muon_step(W, G, M, LR, BETA, NS_STEPS, COEFFS)
+        for _ in range(10):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        replay = steps / (time.perf_counter() - t0)
+        out[name] = {"matrices": len(specs), "params": sum(s.rows * s.cols for s in specs),
+                     "eager_steps_per_s": round(eager, 1), "graph_replay_steps_per_s": round(replay, 1)}
+        del W, G, M, graph
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -137,6 +175,8 @@ def main():
     ap.add_argument("--no-kernel-breakdown", action="store_true",
                     help="skip the per-kernel-family timing pass after the timed region")
     ap.add_argument("--no-adamw", action="store_true", help="skip the AdamW measurement after the timed region")
+    ap.add_argument("--no-small", action="store_true",
+                    help="skip the small-workload (eager vs graph replay) measurement after the timed region")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -229,6 +269,7 @@ def main():
                                "frac_bf16_peak": round(ns_tf / PEAK_BF16_TFLOPS, 4)}
 
     adamw = None if args.no_adamw else bench_adamw(torch, mu, wl)
+    small = None if args.no_small else bench_small(torch, mu, wl)
 
     # A plain copy of known size, outside the timed region: it calibrates
     # rocprofv3's FETCH_SIZE / WRITE_SIZE counters when this script is profiled.
@@ -279,6 +320,8 @@ def main():
         out["kernels"] = breakdown
     if adamw is not None:
         out["adamw"] = adamw
+    if small is not None:
+        out["small_workloads"] = small
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_budget)
     print(json.dumps(out), flush=True)

@@ -35,6 +35,10 @@
  *     Kernel faults surface at the caller's next synchronisation.  Calls that
  *     overlap in time on one device must use the same stream (they share the
  *     library's workspace).
+ *   - After the first call with a given set of pointers and shapes (which
+ *     builds and caches the plan, and synchronises once), a call only
+ *     enqueues kernel launches: no allocation, no copy, no synchronisation,
+ *     no memset.  Such calls can be captured into a HIP graph and replayed.
  *   - Arguments are validated on the host before any HIP call; on failure
  *     the call returns a negative code, enqueues nothing and
  *     muon_last_error() describes the problem.
@@ -90,7 +94,9 @@ int muon_step(float* const* params, const float* const* grads, float* const* mom
  * Same as muon_step, and additionally writes the bf16 update X (the value
  * applied as W -= lr * X) to updates[i] (uint16 bf16 bit patterns,
  * rows x cols, caller orientation).  updates may be NULL, or any element may
- * be NULL, to skip that output.
+ * be NULL, to skip that output.  The update pointers are part of the cached
+ * plan's key: passing new update buffers every call builds a new plan (with
+ * a synchronisation) every call, so reuse them.
  */
 int muon_step_ex(float* const* params, const float* const* grads, float* const* momentum,
                  const muon_shape_t* shapes, int n, float lr, float beta, int ns_steps,

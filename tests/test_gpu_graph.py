@@ -1,0 +1,84 @@
+"""Graph capture: once a pointer set's plan is cached, a step only enqueues
+kernel launches, so it can be captured into a HIP graph and replayed.  Each
+replay must equal the eager step on copies of the same state, bit for bit,
+with eager work and synchronisations between the replays."""
+import numpy as np
+import pytest
+
+from gpu_helpers import COEFFS, say, to_gpu, torch_mod
+from optimizer_muon_step_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = torch_mod()
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import optimizer_muon_step_amd as mu
+    mu._lib.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def test_captured_muon_step_replays_like_eager():
+    torch = torch_mod()
+    import optimizer_muon_step_amd as mu
+    mats = [wl.make_matrix("c2", i, 4) for i in range(4)]
+    W = [to_gpu(m["W"]) for m in mats]
+    M = [to_gpu(m["buf"]) for m in mats]
+    G = [to_gpu(m["grads"][0]) for m in mats]
+    We = [w.clone() for w in W]
+    Me = [m.clone() for m in M]
+    Ge = [g.clone() for g in G]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        mu.muon_step(W, G, M, 0.02, 0.95, 5, COEFFS)  # builds and caches the plan for these pointers
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    mu.muon_step(We, Ge, Me, 0.02, 0.95, 5, COEFFS)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        mu.muon_step(W, G, M, 0.02, 0.95, 5, COEFFS)
+    for rep in range(1, 4):
+        # new gradients in place, eager work between replays
+        for i, m in enumerate(mats):
+            G[i].copy_(to_gpu(m["grads"][rep]))
+            Ge[i].copy_(G[i])
+        graph.replay()
+        mu.muon_step(We, Ge, Me, 0.02, 0.95, 5, COEFFS)
+        torch.cuda.synchronize()
+        for a, b in zip(W + M, We + Me):
+            assert torch.equal(a, b), f"replay {rep} differs from the eager step"
+        say(f"  replay {rep}: bit-identical to eager")
+
+
+def test_captured_adamw_step_replays_like_eager():
+    torch = torch_mod()
+    import optimizer_muon_step_amd as mu
+    rng = np.random.default_rng(40)
+    sizes = [768, 4099, 50257]
+    P = [to_gpu(rng.standard_normal(n).astype(np.float32)) for n in sizes]
+    G = [to_gpu(rng.standard_normal(n).astype(np.float32)) for n in sizes]
+    U = [torch.zeros(n, device="cuda") for n in sizes]
+    V = [torch.zeros(n, device="cuda") for n in sizes]
+    Pe, Ge, Ue, Ve = ([t.clone() for t in L] for L in (P, G, U, V))
+    wds = [0.0, 0.1, 0.1]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        mu.muon_adamw_step(P, G, U, V, 1e-3, weight_decay=wds, step=1)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    mu.muon_adamw_step(Pe, Ge, Ue, Ve, 1e-3, weight_decay=wds, step=1)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        mu.muon_adamw_step(P, G, U, V, 1e-3, weight_decay=wds, step=2)  # step is baked into the capture
+    for rep in range(3):
+        graph.replay()
+        mu.muon_adamw_step(Pe, Ge, Ue, Ve, 1e-3, weight_decay=wds, step=2)
+        torch.cuda.synchronize()
+        for a, b in zip(P + U + V, Pe + Ue + Ve):
+            assert torch.equal(a, b), f"replay {rep} differs from the eager step"
