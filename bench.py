@@ -127,6 +127,48 @@ def bench_adamw(torch, mu, wl, calls=50):
     }
 
 
+def bench_vendor_ns(torch, wl, ns_flops_step, steps=20):
+    """The same 5 Newton-Schulz iterations on the same 48 canonical bf16
+    matrices done the stock way, with torch bf16 matmuls (hipBLASLt) per
+    shape group, for comparison with the library's NS kernels.  Not part of
+    the step; every right operand is made contiguous first (no transposed
+    views in batched bf16 products)."""
+    specs = wl.config_specs(WORKLOAD)
+    groups = {}
+    for s in specs:
+        m, n = min(s.rows, s.cols), max(s.rows, s.cols)
+        groups[(m, n)] = groups.get((m, n), 0) + 1
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    Xs = [(torch.randn((b, m, n), generator=gen, device="cuda") / (m * n) ** 0.5).to(torch.bfloat16)
+          for (m, n), b in groups.items()]
+    a, b, c = COEFFS
+
+    def ns(X):
+        for _ in range(NS_STEPS):
+            Xt = X.transpose(1, 2).contiguous()
+            A = torch.bmm(X, Xt)
+            B = b * A + c * torch.bmm(A, A)
+            X = a * X + torch.bmm(B, X)
+        return X
+
+    for _ in range(3):
+        for X in Xs:
+            ns(X)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        for X in Xs:
+            ns(X)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"what": "5 NS iterations on the 48 c3 matrices with torch bf16 bmm (hipBLASLt) and torch "
+                    "elementwise ops, per shape group; the transposed operand copied contiguous first",
+            "ms_per_step": round(ms, 4), "TFLOP/s_algorithmic": round(ns_flops_step / (ms * 1e-3) / 1e12, 1)}
+
+
 def bench_small(torch, mu, wl, steps=200):
     """Small workloads, where launch overhead matters: steps/s of eager calls
     and of the same step captured once into a HIP graph and replayed."""
@@ -175,6 +217,8 @@ def main():
     ap.add_argument("--no-kernel-breakdown", action="store_true",
                     help="skip the per-kernel-family timing pass after the timed region")
     ap.add_argument("--no-adamw", action="store_true", help="skip the AdamW measurement after the timed region")
+    ap.add_argument("--no-vendor", action="store_true",
+                    help="skip the torch/hipBLASLt Newton-Schulz comparison after the timed region")
     ap.add_argument("--no-small", action="store_true",
                     help="skip the small-workload (eager vs graph replay) measurement after the timed region")
     args = ap.parse_args()
@@ -270,6 +314,7 @@ def main():
 
     adamw = None if args.no_adamw else bench_adamw(torch, mu, wl)
     small = None if args.no_small else bench_small(torch, mu, wl)
+    vendor = None if args.no_vendor else bench_vendor_ns(torch, wl, ns_flops_step)
 
     # A plain copy of known size, outside the timed region: it calibrates
     # rocprofv3's FETCH_SIZE / WRITE_SIZE counters when this script is profiled.
@@ -322,6 +367,11 @@ def main():
         out["adamw"] = adamw
     if small is not None:
         out["small_workloads"] = small
+    if vendor is not None:
+        if breakdown is not None:
+            vendor["library_ns_ms_per_step"] = breakdown["ns_all"]["ms_per_step"]
+            vendor["speedup_of_library"] = round(vendor["ms_per_step"] / breakdown["ns_all"]["ms_per_step"], 2)
+        out["vendor_ns_baseline"] = vendor
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_budget)
     print(json.dumps(out), flush=True)
