@@ -18,7 +18,10 @@
 // NSTAGE-1 slices are in flight while one is multiplied, and every row
 // segment fetched is a whole 128-byte line.  Each lane's 16-byte DMA slot is
 // fixed by its lane id, so a tile's XOR swizzle is applied on the global side
-// (each lane fetches the chunk that belongs in its slot).  k-contiguous tiles
+// (each lane fetches the chunk that belongs in its slot).  UPDATE blocks are
+// persistent, one per CU: while a tile's epilogue stages and stores its
+// output, the first K slice of the block's next tile is already on its way
+// into the other stage.  k-contiguous tiles
 // (X for GRAM, A for POLY, B for UPDATE) feed MFMA fragments with
 // ds_read_b128; the k-major X tile of UPDATE is read with ds_read_b64_tr_b16
 // (see read_tr_frags).  The swizzles assume gfx950's LDS of 64 four-byte
@@ -114,10 +117,17 @@ __device__ __forceinline__ void read_tr_frags4(bf16x8* bfr, const uint32_t* a) {
 
 }  // namespace
 
+// State a block carries from one of its tiles to the next.
+struct TileCarry {
+  bool pre;        // slice 0 of the next tile is already in flight into stage 0
+  bool prev_full;  // the previous tile issued all of its copy-out stores
+};
+
+// One output tile: work item idx of the list (not a padding item).
 template <int KIND, int BM, int BN, int WAVES_M, int WAVES_N, int NSTAGE, int ROWU, int BK>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const MatDesc* __restrict__ descs,
-                                                                        const GemmItem* __restrict__ items,
-                                                                        int src, float ca, float cb, float cc) {
+__device__ __forceinline__ void ns_gemm_tile(const MatDesc* __restrict__ descs, const GemmItem* __restrict__ items,
+                                             int n_items, int idx, int src, float ca, float cb, float cc,
+                                             TileCarry& carry) {
   constexpr int NT = 64 * WAVES_M * WAVES_N;   // threads
   constexpr bool NN = (KIND == GEMM_UPDATE);   // B operand stored k-major
   constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;  // wave tile
@@ -139,10 +149,19 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const M
                 "UPDATE tiling: 32-row blocks of the tile each inside one K slice");
   static_assert(NN || ROWU == BM, "symmetric tiles are addressed in units of their own size");
   static_assert(!NN || BN >= 128, "k-major swizzle needs 16 chunks per row");
-  __shared__ __attribute__((aligned(16))) char lds[NSTAGE * STAGE_BYTES];
+  // UPDATE blocks are persistent (one per CU, each walking its tiles) and
+  // fetch the next tile's first K slice into stage 0 while the current tile's
+  // epilogue runs, so the staged output tile lives past stage 0.
+  constexpr bool PF = NN;
+  static_assert(!PF || NSTAGE == 2, "cross-tile prefetch: the last slice of a tile sits in stage 1");
+  constexpr int E_OFF = PF ? STAGE_BYTES : 0;  // byte offset of the staged output tile
+  constexpr int LDS_BYTES = (E_OFF + BM * BN * 2 > NSTAGE * STAGE_BYTES) ? E_OFF + BM * BN * 2 : NSTAGE * STAGE_BYTES;
+  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  // byte offsets of slice s's A and B operand buffers
+  auto a_off = [](int s) { return (s % NSTAGE) * STAGE_BYTES; };
+  auto b_off = [](int s) { return (s % NSTAGE) * STAGE_BYTES + A_BYTES; };
 
-  const GemmItem it = items[blockIdx.x];
-  if (it.mat < 0) return;  // padding item of a shorter per-XCD run
+  const GemmItem it = items[idx];
   const MatDesc& d = descs[it.mat];
   const uint16_t* Aop;
   const uint16_t* Bop;
@@ -168,7 +187,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const M
   // the same time and share them in L2.
   auto kt_of = [&](int s) { return s; };
 
-  const int tid = threadIdx.x;
+  // In the persistent UPDATE loop an opaque zero makes lane-derived offsets
+  // be recomputed per tile instead of hoisted out of the loop, where they
+  // would stay live across it.
+  int opq0 = 0;
+  if constexpr (PF) asm volatile("v_mov_b32 %0, 0" : "=v"(opq0));
+  const int tid = threadIdx.x + opq0;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wi = wave / WAVES_N, wj = wave % WAVES_N;
@@ -198,7 +222,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const M
   const bool same_rows = !NN && row0 == col0;
   auto issue = [&](int s) {
     const int kt = kt_of(s);
-    LDS_AS char* st = (LDS_AS char*)lds + (s % NSTAGE) * STAGE_BYTES;
+    LDS_AS char* st = (LDS_AS char*)lds + a_off(s);
 #pragma unroll
     for (int q = 0; q < A_INSTR; ++q) {
       const int g = wave * A_INSTR + q;
@@ -219,6 +243,31 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const M
         src_row = Bop + (int64_t)(col0 + g * RPI) * ldb + (int64_t)kt * BK;
         vo = b_vo[g & 1];
       }
+      __builtin_amdgcn_global_load_lds((const void*)(src_row + vo), (LDS_AS void*)(st + A_BYTES + g * 1024), 16, 0, 0);
+    }
+  };
+  // slice 0 of another UPDATE tile of this call into stage 0
+  auto issue_first = [&](const GemmItem& nit) {
+    const MatDesc& nd = descs[nit.mat];
+    const uint16_t* nA = nd.B;
+    const uint16_t* nB = nd.X[src];
+    const int nlda = nd.ld_a, nldb = nd.ld_x;
+    const int nrow0 = nit.ti * ROWU, ncol0 = nit.tj * BN;
+    LDS_AS char* st = (LDS_AS char*)lds;
+#pragma unroll
+    for (int q = 0; q < A_INSTR; ++q) {
+      const int g = wave * A_INSTR + q;
+      const int row = (g & 1) * RPI + lane / CPR;
+      const int vo = (lane / CPR) * nlda + swz_k<BK>(row, lane % CPR) * 8;
+      const uint16_t* src_row = nA + (int64_t)(nrow0 + g * RPI) * nlda;
+      __builtin_amdgcn_global_load_lds((const void*)(src_row + vo), (LDS_AS void*)(st + g * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < B_INSTR; ++q) {
+      const int g = wave * B_INSTR + q;
+      const int row = g * (64 / NCHUNK_N) + lane / NCHUNK_N;
+      const uint16_t* src_row = nB + (int64_t)(g * (64 / NCHUNK_N)) * nldb + ncol0;
+      const int vo = (lane / NCHUNK_N) * nldb + swz_n(row, lane % NCHUNK_N) * 8;
       __builtin_amdgcn_global_load_lds((const void*)(src_row + vo), (LDS_AS void*)(st + A_BYTES + g * 1024), 16, 0, 0);
     }
   };
@@ -251,7 +300,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const M
       for (int h = 0; h < 2; ++h) {
         const int k = 8 * (g >> 1) + 4 * h + (l16 >> 2);
         const int j = wj * WTN + nj * 32 + 16 * (g & 1) + 4 * (l16 & 3);
-        b_rd[nj][h] = A_BYTES + k * (BN * 2) + swz_n(k, j >> 3) * 16 + (j & 7) * 2;
+        b_rd[nj][h] = k * (BN * 2) + swz_n(k, j >> 3) * 16 + (j & 7) * 2;  // within the X slice
       }
     }
   }
@@ -288,8 +337,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const M
   };
 
   auto compute = [&](int s) {
-    const LDS_AS char* st = (const LDS_AS char*)lds + (s % NSTAGE) * STAGE_BYTES;
-    const uint32_t st_addr = (uint32_t)(uintptr_t)st;
+    const LDS_AS char* st = (const LDS_AS char*)lds + a_off(s);
+    const uint32_t st_addr = (uint32_t)(uintptr_t)((const LDS_AS char*)lds + b_off(s));
     if constexpr (!NN) {
 #pragma unroll
       for (int kk = 0; kk < BK / 16; ++kk) {
@@ -338,7 +387,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const M
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) ein[mi][nj][e4] = u32x2{0u, 0u};
   auto capture_poly = [&](int s) {
-    const LDS_AS char* st = (const LDS_AS char*)lds + (s % NSTAGE) * STAGE_BYTES;
+    const LDS_AS char* st = (const LDS_AS char*)lds + a_off(s);
     const int kt = kt_of(s);
 #pragma unroll
     for (int nj = 0; nj < TN; ++nj) {
@@ -354,10 +403,19 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const M
         }
     }
   };
+  // With the cross-tile prefetch the LDS past the two stages is idle during
+  // the K loop; the a.X values of each wave's last 32-row block wait there
+  // (in register order, 8 bytes a lane) instead of in registers.
+  constexpr int PARK_OFF = NSTAGE * STAGE_BYTES;
+  constexpr int PARK_MI = PF ? TM - 1 : TM;  // TM: nothing parked
+  static_assert(!PF || PARK_OFF + (NT / 64) * TN * 4 * 512 <= LDS_BYTES, "parking space");
+  auto park_addr = [&](int nj, int e4) {
+    return (LDS_AS char*)lds + PARK_OFF + ((wave * TN + nj) * 4 + e4) * 512 + lane * 8;
+  };
   auto capture_update = [&](int s) {
     // slice s holds X rows s*BK .. s*BK+BK-1; a 32-row block of output rows
     // lies inside one slice (rows past m_pad fall in none and are not stored)
-    const LDS_AS char* slice = (const LDS_AS char*)lds + (s % NSTAGE) * STAGE_BYTES + A_BYTES;
+    const LDS_AS char* slice = (const LDS_AS char*)lds + b_off(s);
     const int kt = kt_of(s);
 #pragma unroll
     for (int mi = 0; mi < TM; ++mi) {
@@ -369,7 +427,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const M
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) {
           const int cl = wj * WTN + nj * 32 + 8 * e4 + 4 * (lane >> 5);
-          ein[mi][nj][e4] = *(const LDS_AS u32x2*)(slice + lr * (BN * 2) + swz_n(lr, cl >> 3) * 16 + (cl & 7) * 2);
+          const u32x2 xv = *(const LDS_AS u32x2*)(slice + lr * (BN * 2) + swz_n(lr, cl >> 3) * 16 + (cl & 7) * 2);
+          if (mi == PARK_MI)
+            *(LDS_AS u32x2*)park_addr(nj, e4) = xv;
+          else
+            ein[mi][nj][e4] = xv;
         }
     }
   };
@@ -379,14 +441,22 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const M
   // x LPW DMA operations outstanding and every wave has passed the barrier;
   // the buffer refilled next was last read in step s-1, which every wave
   // finished (its LDS reads included) before the barrier.
+  if (!carry.pre) {
 #pragma unroll
-  for (int s = 0; s < NSTAGE - 1; ++s)
-    if (s < KT) issue(s);
+    for (int s = 0; s < NSTAGE - 1; ++s)
+      if (s < KT) issue(s);
+  }
+  constexpr int NSTORE = BM * (BN / 8) / NT;  // copy-out stores per lane
   for (int s = 0; s < KT; ++s) {
     // slices issued after s: min(NSTAGE - 2, KT - 1 - s), each LPW transfers
     // per wave (A_INSTR on a diagonal tile, which fetches one operand)
     const int after = min(NSTAGE - 2, KT - 1 - s);
-    if (after >= 2 && NSTAGE >= 4) {
+    if (PF && s == 0 && carry.pre) {
+      // slice 0 went out before the previous tile's copy-out stores; vector
+      // memory operations complete in order, so it has landed once at most
+      // those stores remain
+      if (carry.prev_full) wait_vm_lgkm0<NSTORE>(); else wait_vm_lgkm0<0>();
+    } else if (after >= 2 && NSTAGE >= 4) {
       if (same_rows) wait_vm_lgkm0<2 * A_INSTR>(); else wait_vm_lgkm0<2 * LPW>();
     } else if (after >= 1 && NSTAGE >= 3) {
       if (same_rows) wait_vm_lgkm0<A_INSTR>(); else wait_vm_lgkm0<LPW>();
@@ -409,11 +479,26 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const M
   wait_vm_lgkm0<0>();
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-  LDS_AS char* E = (LDS_AS char*)lds;
+  bool has_next = false;
+  if constexpr (PF) {
+    int nidx = idx + gridDim.x;
+    while (nidx < n_items && items[nidx].mat < 0) nidx += gridDim.x;
+    has_next = nidx < n_items && (KT % 2 == 0);  // stage 0 is free: the last slice sits in stage 1
+    if (has_next) issue_first(items[nidx]);
+    // collect the parked a.X values before the staged tile overwrites them
+#pragma unroll
+    for (int nj = 0; nj < TN; ++nj)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) ein[PARK_MI][nj][e4] = *(const LDS_AS u32x2*)park_addr(nj, e4);
+    wait_vm_lgkm0<63>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  }
+  LDS_AS char* E = (LDS_AS char*)lds + E_OFF;
   constexpr int ROWB = BN * 2;          // staged row bytes
   constexpr int RCH = BN / 8;           // 16-byte chunks per staged row
   static_assert(KIND == GEMM_UPDATE || BM == BN, "symmetric tiles are square");
-  static_assert(BM * ROWB <= NSTAGE * STAGE_BYTES, "staging does not fit");
+  static_assert(BM * ROWB <= LDS_BYTES, "staging does not fit");
   static_assert(RCH >= 16, "staging swizzle needs 16 chunks per row");
   // Chunk swizzle of a staged row.  Copy-out reads 16 lanes along one row
   // (any XOR keeps them distinct); the transposing reads of the mirror put a
@@ -443,7 +528,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const M
       }
     }
   }
-  wait_vm_lgkm0<0>();
+  if constexpr (PF) wait_vm_lgkm0<63>(); else wait_vm_lgkm0<0>();  // LDS only: the prefetch stays in flight
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   constexpr int CHUNKS = BM * RCH;
@@ -496,6 +581,30 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const M
       *reinterpret_cast<MUON_GLOBAL u32x4*>(C + (int64_t)(col0 + j) * ldc + row0 + k0) = val;
     }
   }
+  if constexpr (PF) {
+    __syncthreads();  // staged-tile reads finish before the next tile refills the ring
+    carry.pre = has_next;
+    carry.prev_full = row0 + BM <= row_lim;
+  }
+}
+
+template <int KIND, int BM, int BN, int WAVES_M, int WAVES_N, int NSTAGE, int ROWU, int BK>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const MatDesc* __restrict__ descs,
+                                                                        const GemmItem* __restrict__ items,
+                                                                        int src, float ca, float cb, float cc, int n_items) {
+  TileCarry carry{false, false};
+  if constexpr (KIND == GEMM_UPDATE) {
+    // UPD_BLOCKS persistent blocks: block b takes items b, b + gridDim.x, ...,
+    // all planned for XCD b % 8 (gridDim.x is a multiple of 8 or n_items)
+    for (int idx = blockIdx.x; idx < n_items; idx += gridDim.x) {
+      if (items[idx].mat < 0) continue;  // padding item of a shorter per-XCD run
+      ns_gemm_tile<KIND, BM, BN, WAVES_M, WAVES_N, NSTAGE, ROWU, BK>(descs, items, n_items, idx, src, ca, cb, cc, carry);
+    }
+  } else {
+    if (items[blockIdx.x].mat < 0) return;  // padding item of a shorter per-XCD run
+    ns_gemm_tile<KIND, BM, BN, WAVES_M, WAVES_N, NSTAGE, ROWU, BK>(descs, items, n_items, blockIdx.x, src, ca, cb, cc,
+                                                                   carry);
+  }
 }
 
 hipError_t launch_gemm(int kind, const MatDesc* d, const GemmItem* items, int n_items, int src,
@@ -503,13 +612,13 @@ hipError_t launch_gemm(int kind, const MatDesc* d, const GemmItem* items, int n_
   if (n_items == 0) return hipSuccess;
   switch (kind) {
     case GEMM_GRAM:
-      ns_gemm_kernel<GEMM_GRAM, GRAM_BM, GRAM_BM, 2, 4, 2, GRAM_BM, 64><<<n_items, 512, 0, s>>>(d, items, src, ca, cb, cc);
+      ns_gemm_kernel<GEMM_GRAM, GRAM_BM, GRAM_BM, 2, 4, 2, GRAM_BM, 64><<<n_items, 512, 0, s>>>(d, items, src, ca, cb, cc, n_items);
       break;
     case GEMM_POLY:
-      ns_gemm_kernel<GEMM_POLY, SYM_BM, SYM_BN, 2, 4, SYM_NSTAGE, SYM_BM, SYM_BK><<<n_items, 512, 0, s>>>(d, items, src, ca, cb, cc);
+      ns_gemm_kernel<GEMM_POLY, SYM_BM, SYM_BN, 2, 4, SYM_NSTAGE, SYM_BM, SYM_BK><<<n_items, 512, 0, s>>>(d, items, src, ca, cb, cc, n_items);
       break;
     default:
-      ns_gemm_kernel<GEMM_UPDATE, UPD_BM, UPD_BN, 2, 4, 2, UPD_ROWU, 64><<<n_items, 512, 0, s>>>(d, items, src, ca, cb, cc);
+      ns_gemm_kernel<GEMM_UPDATE, UPD_BM, UPD_BN, 2, 4, 2, UPD_ROWU, 64><<<n_items < UPD_BLOCKS ? n_items : UPD_BLOCKS, 512, 0, s>>>(d, items, src, ca, cb, cc, n_items);
       break;
   }
   return hipGetLastError();

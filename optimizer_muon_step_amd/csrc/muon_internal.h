@@ -14,6 +14,9 @@ constexpr int SYM_BM = 128, SYM_BN = 128;  // POLY output tile
 constexpr int SYM_BK = 64, SYM_NSTAGE = 2;  // GRAM / POLY K slice and ring depth (measured best)
 constexpr int UPD_BM = 192, UPD_BN = 256;  // UPDATE output tile (rows may overhang m_pad)
 constexpr int UPD_ROWU = 64;               // UPDATE tile rows start at multiples of this
+// Persistent UPDATE grid: one block per CU of the 256 (8 XCDs x 32); a
+// multiple of 8 so that every tile a block takes was planned for its XCD.
+constexpr int UPD_BLOCKS = 256;
 constexpr int NS_PAD_M = 256;              // multiple of GRAM_BM and SYM_BM
 constexpr int NS_PAD_N = 256;              // multiple of UPD_BN
 constexpr int NS_THREADS = 256;

@@ -88,9 +88,11 @@ def cmd_trace(args):
         sel = trace[first:first + count]
         if len(sel) != count:
             raise SystemExit(f"window {w}: only {len(sel)} launches")
-        mean = sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in sel) / count / 1e3
+        durs = sorted((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in sel)
+        mean = sum(durs) / count
+        median = (durs[(count - 1) // 2] + durs[count // 2]) / 2
         lines += ["", f"{fam} launches {first + 1}-{first + count} (in dispatch order; the benchmark's timed "
-                      f"region): mean {mean:.2f} us over {count} launches."]
+                      f"region): mean {mean:.2f} us, median {median:.2f} us over {count} launches."]
     open(args.out, "w").write("\n".join(lines) + "\n")
 
 
