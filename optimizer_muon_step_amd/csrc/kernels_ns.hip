@@ -24,7 +24,7 @@
 // into the other stage.  k-contiguous tiles
 // (X for GRAM, A for POLY, B for UPDATE) feed MFMA fragments with
 // ds_read_b128; the k-major X tile of UPDATE is read with ds_read_b64_tr_b16
-// (see read_tr_frags).  The swizzles assume gfx950's LDS of 64 four-byte
+// (see read_tr_frag).  The swizzles assume gfx950's LDS of 64 four-byte
 // banks.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -74,45 +74,14 @@ __device__ __forceinline__ int swz_n(int row, int chunk) { return chunk ^ (4 * (
 // per 32-column fragment (ds_read_b64_tr_b16 transposes 16-bit elements
 // across each group of 16 lanes: with lane L of a group addressing row
 // k0 + L/4, columns j0 + 4(L%4) .. +3, lane i of the group receives column
-// j0 + i, rows k0 .. k0+3).  They are issued from inline assembly because the
-// compiler would otherwise wait for every in-flight global->LDS transfer,
-// later pipeline stages included, before each such read.  The block ends with
-// its own wait, so every output is complete when the block retires; outputs
-// are early-clobber so no output register aliases an address input.
-__device__ __forceinline__ void read_tr_frags2(bf16x8* bfr, uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3) {
-  uint64_t r0, r1, r2, r3;
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %4\n\t"
-      "ds_read_b64_tr_b16 %1, %5\n\t"
-      "ds_read_b64_tr_b16 %2, %6\n\t"
-      "ds_read_b64_tr_b16 %3, %7\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
-      : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
-      : "memory");
-  bfr[0] = __builtin_bit_cast(bf16x8, u32x4{(uint32_t)r0, (uint32_t)(r0 >> 32), (uint32_t)r1, (uint32_t)(r1 >> 32)});
-  bfr[1] = __builtin_bit_cast(bf16x8, u32x4{(uint32_t)r2, (uint32_t)(r2 >> 32), (uint32_t)r3, (uint32_t)(r3 >> 32)});
-}
-
-__device__ __forceinline__ void read_tr_frags4(bf16x8* bfr, const uint32_t* a) {
-  uint64_t r[8];
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %8\n\t"
-      "ds_read_b64_tr_b16 %1, %9\n\t"
-      "ds_read_b64_tr_b16 %2, %10\n\t"
-      "ds_read_b64_tr_b16 %3, %11\n\t"
-      "ds_read_b64_tr_b16 %4, %12\n\t"
-      "ds_read_b64_tr_b16 %5, %13\n\t"
-      "ds_read_b64_tr_b16 %6, %14\n\t"
-      "ds_read_b64_tr_b16 %7, %15\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
-      : "memory");
-#pragma unroll
-  for (int nj = 0; nj < 4; ++nj)
-    bfr[nj] = __builtin_bit_cast(bf16x8, u32x4{(uint32_t)r[2 * nj], (uint32_t)(r[2 * nj] >> 32),
-                                               (uint32_t)r[2 * nj + 1], (uint32_t)(r[2 * nj + 1] >> 32)});
+// j0 + i, rows k0 .. k0+3).  The compiler waits for these reads where their
+// results are used and, in this kernel, inserts no wait for the in-flight
+// global -> LDS transfers before them (checked in the generated code).
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x8 read_tr_frag(uint32_t lo_addr, uint32_t hi_addr) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(uintptr_t)lo_addr);
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(uintptr_t)hi_addr);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 }  // namespace
@@ -315,17 +284,8 @@ __device__ __forceinline__ void ns_gemm_tile(const MatDesc* __restrict__ descs, 
   auto read_b_tr = [&](uint32_t st_addr, int kk, bf16x8* bfr) {
     // k-step kk is 16 rows further on; (row % 4), hence the swizzle, is unchanged
     const uint32_t dk = st_addr + kk * 16 * (BN * 2);
-    if constexpr (TN == 2) {
-      read_tr_frags2(bfr, dk + b_rd[0][0], dk + b_rd[0][1], dk + b_rd[1][0], dk + b_rd[1][1]);
-    } else {
-      uint32_t ad[8];
 #pragma unroll
-      for (int nj = 0; nj < 4; ++nj) {
-        ad[2 * nj] = dk + b_rd[nj][0];
-        ad[2 * nj + 1] = dk + b_rd[nj][1];
-      }
-      read_tr_frags4(bfr, ad);
-    }
+    for (int nj = 0; nj < TN; ++nj) bfr[nj] = read_tr_frag(dk + b_rd[nj][0], dk + b_rd[nj][1]);
   };
   auto mfma_rows = [&](int m0, int m1, const bf16x8* af, const bf16x8* bfr) {
     // operands swapped so each lane ends up with 4 consecutive output columns
@@ -351,7 +311,7 @@ __device__ __forceinline__ void ns_gemm_tile(const MatDesc* __restrict__ descs, 
       }
     } else {
       // Operands of k-step kk+1 are read between the two halves of k-step kk's
-      // MFMAs, so the read block's closing wait overlaps queued MFMA work.  A
+      // MFMAs, so their latency overlaps queued MFMA work.  A
       // fragments: the first half is refreshed for kk+1 once its MFMAs have
       // issued; the second half is read for kk at the start of the step.
       constexpr int MH = (TM + 1) / 2;
@@ -550,7 +510,6 @@ __device__ __forceinline__ void ns_gemm_tile(const MatDesc* __restrict__ descs, 
     // k0 .. k0+3; two reads give 8 rows, one 16-byte piece of a mirrored
     // row.  Group task g covers columns j0 = 16 (g % (BN/16)), rows
     // k0 = 8 (g / (BN/16)); the two groups of a 32-lane half share k0.
-    typedef short s16x4 __attribute__((ext_vector_type(4)));
     constexpr int NGT = (BN / 16) * (BM / 8);
     static_assert(NGT % (NT / 16) == 0, "mirror split");
     const int i16 = tid & 15;
