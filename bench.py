@@ -207,6 +207,64 @@ def bench_small(torch, mu, wl, steps=200):
     return out
 
 
+def bench_large(torch, mu, wl):
+    """The other two named workloads, timed like the headline one (HIP
+    events around whole steps, then per-kernel events for the NS GEMMs):
+    the GPT-2-XL-shaped hidden set (1.47 B params; its inputs are drawn on
+    the device with the c4 distribution, since host generation of 3 B
+    values would dominate the run) and the stress pair (inputs from the
+    seeded generators)."""
+    out = {}
+    for name, warm, steps in (("c5", 5, 20), ("c4", 2, 5)):
+        specs = wl.config_specs(name)
+        shapes = [(s.rows, s.cols) for s in specs]
+        if name == "c4":
+            gen = torch.Generator(device="cuda")
+            gen.manual_seed(4000)
+            W, G = [], []
+            for s in specs:
+                W.append(torch.randn((s.rows, s.cols), device="cuda", generator=gen) * 0.02)
+                G.append(torch.randn((s.rows, s.cols), device="cuda", generator=gen)
+                         * (1e-3 * wl.layer_factor(name, s.layer)))
+        else:
+            W = [torch.from_numpy(wl.make_params(name, i, s)).cuda() for i, s in enumerate(specs)]
+            G = [torch.from_numpy(wl.make_grad(name, i, s, 1)).cuda() for i, s in enumerate(specs)]
+        M = [torch.zeros((s.rows, s.cols), device="cuda") for s in specs]
+        stream = torch.cuda.current_stream()
+
+        def step():
+            mu.muon_step(W, G, M, LR, BETA, NS_STEPS, COEFFS, stream=stream)
+
+        for _ in range(warm):
+            step()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        ns_ms = 0.0
+        for k in (mu.KERNEL_GRAM, mu.KERNEL_POLY, mu.KERNEL_UPDATE):
+            mu.muon_timing_enable(k)
+            for _ in range(2):
+                step()
+            t, cnt = mu.muon_timing_read()
+            mu.muon_timing_enable(-1)
+            ns_ms += t / 2
+        gram_f, poly_f, upd_f = ns_flops(shapes)
+        ns_tf = NS_STEPS * (gram_f + poly_f + upd_f) / (ns_ms * 1e-3) / 1e12
+        out[name] = {"matrices": len(specs), "params": sum(r * c for r, c in shapes),
+                     "steps_per_s": round(1e3 / ms, 2), "ms_per_step": round(ms, 4),
+                     "ns_ms_per_step": round(ns_ms, 4), "ns_TFLOP/s": round(ns_tf, 1),
+                     "ns_frac_bf16_peak": round(ns_tf / PEAK_BF16_TFLOPS, 4)}
+        del W, G, M
+        torch.cuda.synchronize()
+        mu.muon_release()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -221,6 +279,8 @@ def main():
                     help="skip the torch/hipBLASLt Newton-Schulz comparison after the timed region")
     ap.add_argument("--no-small", action="store_true",
                     help="skip the small-workload (eager vs graph replay) measurement after the timed region")
+    ap.add_argument("--no-large", action="store_true",
+                    help="skip the GPT-2-XL-shaped and stress workloads measured after the timed region")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -314,6 +374,7 @@ def main():
 
     adamw = None if args.no_adamw else bench_adamw(torch, mu, wl)
     small = None if args.no_small else bench_small(torch, mu, wl)
+    large = None if args.no_large else bench_large(torch, mu, wl)
     vendor = None if args.no_vendor else bench_vendor_ns(torch, wl, ns_flops_step)
 
     # A plain copy of known size, outside the timed region: it calibrates
@@ -367,6 +428,8 @@ def main():
         out["adamw"] = adamw
     if small is not None:
         out["small_workloads"] = small
+    if large is not None:
+        out["large_workloads"] = large
     if vendor is not None:
         if breakdown is not None:
             vendor["library_ns_ms_per_step"] = breakdown["ns_all"]["ms_per_step"]

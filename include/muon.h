@@ -187,7 +187,8 @@ const char* muon_last_error(void);
 
 /*
  * Device workspace bytes a call over these shapes needs (bf16 iterates,
- * Gram and polynomial matrices, norm partials, work lists).  Pure host
+ * Gram and polynomial matrices, norm partials, fp32 partial tiles when a
+ * long-K Gram product is cut into K chunks, work lists).  Pure host
  * computation.  Returns 0 and sets the error text for invalid shapes.
  */
 size_t muon_workspace_bytes(const muon_shape_t* shapes, int n);

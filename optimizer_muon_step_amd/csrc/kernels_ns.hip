@@ -96,7 +96,7 @@ struct TileCarry {
 template <int KIND, int BM, int BN, int WAVES_M, int WAVES_N, int NSTAGE, int ROWU, int BK>
 __device__ __forceinline__ void ns_gemm_tile(const MatDesc* __restrict__ descs, const GemmItem* __restrict__ items,
                                              int n_items, int idx, int src, float ca, float cb, float cc,
-                                             TileCarry& carry) {
+                                             float* __restrict__ part, TileCarry& carry) {
   constexpr int NT = 64 * WAVES_M * WAVES_N;   // threads
   constexpr bool NN = (KIND == GEMM_UPDATE);   // B operand stored k-major
   constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;  // wave tile
@@ -150,11 +150,14 @@ __device__ __forceinline__ void ns_gemm_tile(const MatDesc* __restrict__ descs, 
   const int row0 = it.ti * ROWU;
   const int col0 = it.tj * BN;  // output columns: rows of Bop (GRAM/POLY), columns of X (UPDATE)
   const int row_lim = d.m_pad;
-  const int KT = K / BK;
-  // K is walked in order, slice s = k-range s*BK .. s*BK+BK-1, by every tile:
-  // the row tiles of one UPDATE column block fetch the same X slices at about
-  // the same time and share them in L2.
-  auto kt_of = [&](int s) { return s; };
+  // A Gram K chunk covers slices k0 .. k0+kn-1 of its tile; every other item
+  // the whole K.
+  const int KT = it.kn > 0 ? it.kn : K / BK;
+  // K is walked in order, slice s = k-range (k0+s)*BK .. +BK-1, by every
+  // tile: the row tiles of one UPDATE column block fetch the same X slices at
+  // about the same time and share them in L2.
+  const int k0 = it.k0;
+  auto kt_of = [&](int s) { return k0 + s; };
 
   // In the persistent UPDATE loop an opaque zero makes lane-derived offsets
   // be recomputed per tile instead of hoisted out of the loop, where they
@@ -433,9 +436,28 @@ __device__ __forceinline__ void ns_gemm_tile(const MatDesc* __restrict__ descs, 
 
   // Epilogue.  Lane holds, for MFMA tile (mi, nj) and quad e4, output row
   // i = wi*WTM + mi*32 + lane%32 and columns j .. j+3 with
-  // j = wj*WTN + nj*32 + 8*e4 + 4*(lane/32) (tile-relative).  Results are
-  // rounded to bf16 and staged in LDS (the pipeline buffers are free now),
-  // then written out as whole 16-byte row segments.
+  // j = wj*WTN + nj*32 + 8*e4 + 4*(lane/32) (tile-relative).
+  if constexpr (KIND == GEMM_GRAM) {
+    if (it.slot >= 0) {
+      // K chunk of a split tile: its fp32 partial sums, unrounded, for the
+      // reduce pass (BM x BN row-major)
+      float* pt = part + (size_t)it.slot * (BM * BN);
+#pragma unroll
+      for (int mi = 0; mi < TM; ++mi)
+#pragma unroll
+        for (int nj = 0; nj < TN; ++nj)
+#pragma unroll
+          for (int e4 = 0; e4 < 4; ++e4) {
+            const int r = wi * WTM + mi * 32 + (lane & 31);
+            const int c = wj * WTN + nj * 32 + 8 * e4 + 4 * (lane >> 5);
+            *reinterpret_cast<float4*>(pt + r * BN + c) = float4{acc[mi][nj][4 * e4], acc[mi][nj][4 * e4 + 1],
+                                                                 acc[mi][nj][4 * e4 + 2], acc[mi][nj][4 * e4 + 3]};
+          }
+      return;
+    }
+  }
+  // Results are rounded to bf16 and staged in LDS (the pipeline buffers are
+  // free now), then written out as whole 16-byte row segments.
   wait_vm_lgkm0<0>();
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
@@ -550,36 +572,114 @@ __device__ __forceinline__ void ns_gemm_tile(const MatDesc* __restrict__ descs, 
 template <int KIND, int BM, int BN, int WAVES_M, int WAVES_N, int NSTAGE, int ROWU, int BK>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const MatDesc* __restrict__ descs,
                                                                         const GemmItem* __restrict__ items,
-                                                                        int src, float ca, float cb, float cc, int n_items) {
+                                                                        int src, float ca, float cb, float cc, int n_items,
+                                                                        float* __restrict__ part) {
   TileCarry carry{false, false};
   if constexpr (KIND == GEMM_UPDATE) {
     // UPD_BLOCKS persistent blocks: block b takes items b, b + gridDim.x, ...,
     // all planned for XCD b % 8 (gridDim.x is a multiple of 8 or n_items)
     for (int idx = blockIdx.x; idx < n_items; idx += gridDim.x) {
       if (items[idx].mat < 0) continue;  // padding item of a shorter per-XCD run
-      ns_gemm_tile<KIND, BM, BN, WAVES_M, WAVES_N, NSTAGE, ROWU, BK>(descs, items, n_items, idx, src, ca, cb, cc, carry);
+      ns_gemm_tile<KIND, BM, BN, WAVES_M, WAVES_N, NSTAGE, ROWU, BK>(descs, items, n_items, idx, src, ca, cb, cc, part,
+                                                                     carry);
     }
   } else {
     if (items[blockIdx.x].mat < 0) return;  // padding item of a shorter per-XCD run
     ns_gemm_tile<KIND, BM, BN, WAVES_M, WAVES_N, NSTAGE, ROWU, BK>(descs, items, n_items, blockIdx.x, src, ca, cb, cc,
-                                                                   carry);
+                                                                   part, carry);
   }
 }
 
 hipError_t launch_gemm(int kind, const MatDesc* d, const GemmItem* items, int n_items, int src,
-                       float ca, float cb, float cc, hipStream_t s) {
+                       float ca, float cb, float cc, float* part, hipStream_t s) {
   if (n_items == 0) return hipSuccess;
   switch (kind) {
     case GEMM_GRAM:
-      ns_gemm_kernel<GEMM_GRAM, GRAM_BM, GRAM_BM, 2, 4, 2, GRAM_BM, 64><<<n_items, 512, 0, s>>>(d, items, src, ca, cb, cc, n_items);
+      ns_gemm_kernel<GEMM_GRAM, GRAM_BM, GRAM_BM, 2, 4, 2, GRAM_BM, 64><<<n_items, 512, 0, s>>>(d, items, src, ca, cb, cc, n_items, part);
       break;
     case GEMM_POLY:
-      ns_gemm_kernel<GEMM_POLY, SYM_BM, SYM_BN, 2, 4, SYM_NSTAGE, SYM_BM, SYM_BK><<<n_items, 512, 0, s>>>(d, items, src, ca, cb, cc, n_items);
+      ns_gemm_kernel<GEMM_POLY, SYM_BM, SYM_BN, 2, 4, SYM_NSTAGE, SYM_BM, SYM_BK><<<n_items, 512, 0, s>>>(d, items, src, ca, cb, cc, n_items, part);
       break;
     default:
-      ns_gemm_kernel<GEMM_UPDATE, UPD_BM, UPD_BN, 2, 4, 2, UPD_ROWU, 64><<<n_items < UPD_BLOCKS ? n_items : UPD_BLOCKS, 512, 0, s>>>(d, items, src, ca, cb, cc, n_items);
+      ns_gemm_kernel<GEMM_UPDATE, UPD_BM, UPD_BN, 2, 4, 2, UPD_ROWU, 64><<<n_items < UPD_BLOCKS ? n_items : UPD_BLOCKS, 512, 0, s>>>(d, items, src, ca, cb, cc, n_items, part);
       break;
   }
+  return hipGetLastError();
+}
+
+// Reduce pass of split Gram tiles: one block per 64x64 sub-tile.  Each
+// element sums its tile's chunk partials in K order in fp32, is rounded once
+// to bf16, and is written at (r, c) and mirrored to (c, r); a diagonal tile
+// keeps the values on and above its diagonal, so A stays exactly symmetric.
+__global__ __launch_bounds__(256) void gram_reduce_kernel(const MatDesc* __restrict__ descs,
+                                                          const RedItem* __restrict__ items,
+                                                          const float* __restrict__ part) {
+  constexpr int T = RED_TILE;
+  __shared__ uint16_t tile[T][T + 2];
+  const RedItem it = items[blockIdx.x];
+  const MatDesc& d = descs[it.mat];
+  MUON_GLOBAL uint16_t* A = gptr(d.A);
+  const int ld = d.ld_a;
+  const int r0 = it.ti * GRAM_BM + it.bi * T, c0 = it.tj * GRAM_BM + it.bj * T;  // of A
+  const int i = threadIdx.x >> 2, j0 = (threadIdx.x & 3) * 16;                    // within the sub-tile
+  const float* src = part + (size_t)it.slot0 * (GRAM_BM * GRAM_BM) + (it.bi * T + i) * GRAM_BM + it.bj * T + j0;
+  float v[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) v[k] = 0.0f;
+  for (int c = 0; c < it.nchunk; ++c) {
+    const float4* p = reinterpret_cast<const float4*>(src + (size_t)c * (GRAM_BM * GRAM_BM));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 t = p[q];
+      v[4 * q] += t.x;
+      v[4 * q + 1] += t.y;
+      v[4 * q + 2] += t.z;
+      v[4 * q + 3] += t.w;
+    }
+  }
+  uint32_t w[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) w[k] = pack_bf16x2(v[2 * k], v[2 * k + 1]);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    tile[i][j0 + 2 * k] = (uint16_t)(w[k] & 0xffffu);
+    tile[i][j0 + 2 * k + 1] = (uint16_t)(w[k] >> 16);
+  }
+  const int r = r0 + i;
+  if (r <= c0 + j0) {
+    // the whole run lies on or above the diagonal
+    *reinterpret_cast<MUON_GLOBAL u32x4*>(A + (int64_t)r * ld + c0 + j0) =
+        u32x4{w[0], w[1], w[2], w[3]};
+    *reinterpret_cast<MUON_GLOBAL u32x4*>(A + (int64_t)r * ld + c0 + j0 + 8) =
+        u32x4{w[4], w[5], w[6], w[7]};
+  } else {
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      if (r <= c0 + j0 + k) A[(int64_t)r * ld + c0 + j0 + k] = tile[i][j0 + k];
+  }
+  __syncthreads();
+  // mirror: row c0 + i of A takes column i of the sub-tile, strictly below
+  // the diagonal
+  const int mr = c0 + i;
+  if (r0 + j0 + 15 < mr) {
+    uint32_t m[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) m[k] = (uint32_t)tile[j0 + 2 * k][i] | ((uint32_t)tile[j0 + 2 * k + 1][i] << 16);
+    *reinterpret_cast<MUON_GLOBAL u32x4*>(A + (int64_t)mr * ld + r0 + j0) = u32x4{m[0], m[1], m[2], m[3]};
+    *reinterpret_cast<MUON_GLOBAL u32x4*>(A + (int64_t)mr * ld + r0 + j0 + 8) = u32x4{m[4], m[5], m[6], m[7]};
+  } else {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int mc = r0 + j0 + k;
+      if (mc < mr) A[(int64_t)mr * ld + mc] = tile[j0 + k][i];
+    }
+  }
+}
+
+hipError_t launch_gram_reduce(const MatDesc* d, const RedItem* items, int n_items, const float* part,
+                              hipStream_t s) {
+  if (n_items == 0) return hipSuccess;
+  gram_reduce_kernel<<<n_items, 256, 0, s>>>(d, items, part);
   return hipGetLastError();
 }
 

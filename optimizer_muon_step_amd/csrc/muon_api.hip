@@ -90,12 +90,48 @@ int check_shapes(const muon_shape_t* shapes, int n) {
   return MUON_OK;
 }
 
+// Long-K Gram split of a call (GRAM_SPLIT_MIN): the chunk length in K
+// slices, 0 when no tile is cut, and the fp32 partial tiles it needs.
+struct GramSplit {
+  int64_t chunk = 0;
+  int64_t slots = 0;
+};
+
+int64_t gram_slices(const Geometry& g) { return g.n_pad / 64; }
+int64_t gram_tiles(const Geometry& g) {
+  const int64_t t = g.m_pad / GRAM_BM;
+  return t * (t + 1) / 2;
+}
+int64_t gram_chunks(int64_t slices, int64_t chunk) {
+  return (chunk && slices > chunk) ? (slices + chunk - 1) / chunk : 1;
+}
+
+GramSplit gram_split_of(const muon_shape_t* shapes, int n) {
+  GramSplit sp;
+  int64_t total = 0, longest = 0;
+  for (int i = 0; i < n; ++i) {
+    const Geometry g = geometry_of(shapes[i]);
+    total += gram_tiles(g) * gram_slices(g);
+    longest = std::max(longest, gram_slices(g));
+  }
+  const int64_t share = std::max<int64_t>(GRAM_SPLIT_MIN, (total + NS_CUS - 1) / NS_CUS);
+  if (longest <= 2 * share) return sp;
+  sp.chunk = share;
+  for (int i = 0; i < n; ++i) {
+    const Geometry g = geometry_of(shapes[i]);
+    const int64_t nc = gram_chunks(gram_slices(g), sp.chunk);
+    if (nc > 1) sp.slots += gram_tiles(g) * nc;
+  }
+  return sp;
+}
+
 size_t workspace_bytes_of(const muon_shape_t* shapes, int n) {
   size_t total = kControlBytes;
   for (int i = 0; i < n; ++i) {
     const Geometry g = geometry_of(shapes[i]);
     total += 2 * g.x_bytes + 2 * g.a_bytes + g.part_bytes;
   }
+  total += align_up((size_t)gram_split_of(shapes, n).slots * GRAM_BM * GRAM_BM * sizeof(float));
   return total;
 }
 
@@ -144,7 +180,9 @@ struct Plan {
   GemmItem* d_gram = nullptr;
   GemmItem* d_poly = nullptr;
   GemmItem* d_upd = nullptr;
-  int n_mom = 0, n_cast = 0, n_apply = 0, n_gram = 0, n_poly = 0, n_upd = 0;
+  RedItem* d_red = nullptr;
+  float* gram_part = nullptr;  // fp32 partial tiles of split Gram tiles (workspace)
+  int n_mom = 0, n_cast = 0, n_apply = 0, n_gram = 0, n_poly = 0, n_upd = 0, n_red = 0;
   ~Plan() {
     if (dev) (void)hipFree(dev);
     if (host) (void)hipHostFree(host);
@@ -246,7 +284,7 @@ std::vector<GemmItem> xcd_interleave(const std::vector<GemmItem>& seq, const std
     std::stable_sort(r.begin(), r.end(), [](const auto& a, const auto& b) { return a.first > b.first; });
     len = std::max(len, r.size());
   }
-  std::vector<GemmItem> out(len * kXcds, GemmItem{-1, 0, 0});
+  std::vector<GemmItem> out(len * kXcds, GemmItem{-1, 0, 0, 0, 0, -1});
   for (int r = 0; r < kXcds; ++r)
     for (size_t k = 0; k < run[r].size(); ++k) out[k * kXcds + r] = run[r][k].second;
   return out;
@@ -334,27 +372,49 @@ int get_plan(DeviceState& st, int mode, int n, const muon_shape_t* shapes, float
   // backwards starts with the lines most likely still in the memory-side
   // cache.
   std::reverse(cast.begin(), cast.end());
+  // Partial tiles of split Gram tiles follow the matrices' buffers.
+  const GramSplit split = gram_split_of(shapes, n);
+  plan->gram_part = carve<float>(cur, (size_t)split.slots * GRAM_BM * GRAM_BM);
   // GEMM tiles.  Per matrix in an order that reuses operands (update: all row
   // tiles of one column block in a row, sharing that block of X; symmetric
   // phases: upper-triangle tiles row by row), then spread over the XCDs.
-  // Gram and poly tiles differ in size (256 and 128).
+  // Gram and poly tiles differ in size (256 and 128); a long-K Gram tile may
+  // be cut into K chunks, each its own item, summed by the reduce pass.
   std::vector<GemmItem> gram_seq, poly_seq, upd_seq;
+  std::vector<RedItem> red;
   std::vector<int64_t> gram_cost, upd_cost;
+  int32_t slot = 0;
   for (int i = 0; i < n; ++i) {
     const int tg = desc[i].m_pad / GRAM_BM, tm = desc[i].m_pad / SYM_BM, tn = desc[i].n_pad / UPD_BN;
+    const int64_t ks = desc[i].n_pad / 64;
+    const int64_t nc = gram_chunks(ks, split.chunk);
     for (int ti = 0; ti < tg; ++ti)
       for (int tj = ti; tj < tg; ++tj) {
-        gram_seq.push_back({i, (int16_t)ti, (int16_t)tj});
-        gram_cost.push_back(desc[i].n_pad);
+        if (nc == 1) {
+          gram_seq.push_back({i, (int16_t)ti, (int16_t)tj, 0, 0, -1});
+          gram_cost.push_back(ks);
+          continue;
+        }
+        for (int64_t c = 0; c < nc; ++c) {
+          const int64_t a = ks * c / nc, b = ks * (c + 1) / nc;
+          gram_seq.push_back({i, (int16_t)ti, (int16_t)tj, (int32_t)a, (int32_t)(b - a), slot + (int32_t)c});
+          gram_cost.push_back(b - a);
+        }
+        constexpr int SUB = GRAM_BM / RED_TILE;
+        for (int bi = 0; bi < SUB; ++bi)
+          for (int bj = 0; bj < SUB; ++bj)
+            if (ti != tj || bi <= bj) red.push_back({i, (int16_t)ti, (int16_t)tj, slot, (int16_t)nc, (int8_t)bi, (int8_t)bj});
+        slot += (int32_t)nc;
       }
     for (int ti = 0; ti < tm; ++ti)
-      for (int tj = ti; tj < tm; ++tj) poly_seq.push_back({i, (int16_t)ti, (int16_t)tj});
+      for (int tj = ti; tj < tm; ++tj) poly_seq.push_back({i, (int16_t)ti, (int16_t)tj, 0, 0, -1});
     for (int tj = 0; tj < tn; ++tj)
       for (int ti = 0; ti < desc[i].m_pad / UPD_ROWU; ti += UPD_BM / UPD_ROWU) {
-        upd_seq.push_back({i, (int16_t)ti, (int16_t)tj});
+        upd_seq.push_back({i, (int16_t)ti, (int16_t)tj, 0, 0, -1});
         upd_cost.push_back(desc[i].m_pad);
       }
   }
+  if (slot != split.slots) return fail(MUON_EINVAL, "internal: %d Gram partial tiles planned, %lld sized", slot, (long long)split.slots);
   std::vector<int64_t> poly_cost(poly_seq.size());
   for (size_t k = 0; k < poly_seq.size(); ++k) poly_cost[k] = desc[poly_seq[k].mat].m_pad;
   gram = xcd_interleave(gram_seq, gram_cost);
@@ -370,6 +430,7 @@ int get_plan(DeviceState& st, int mode, int n, const muon_shape_t* shapes, float
   const size_t o_gram = place(sizeof(GemmItem) * gram.size());
   const size_t o_poly = place(sizeof(GemmItem) * poly.size());
   const size_t o_upd = place(sizeof(GemmItem) * updl.size());
+  const size_t o_red = place(sizeof(RedItem) * red.size());
   plan->bytes = std::max<size_t>(off, kAlign);
   hipError_t e;
   if ((e = hipHostMalloc(&plan->host, plan->bytes, hipHostMallocDefault)) != hipSuccess) {
@@ -389,6 +450,7 @@ int get_plan(DeviceState& st, int mode, int n, const muon_shape_t* shapes, float
   memcpy(h + o_gram, gram.data(), sizeof(GemmItem) * gram.size());
   memcpy(h + o_poly, poly.data(), sizeof(GemmItem) * poly.size());
   memcpy(h + o_upd, updl.data(), sizeof(GemmItem) * updl.size());
+  memcpy(h + o_red, red.data(), sizeof(RedItem) * red.size());
   if ((e = hipMemcpyAsync(plan->dev, plan->host, plan->bytes, hipMemcpyHostToDevice, stream)) != hipSuccess)
     return fail_hip(e, "hipMemcpyAsync(plan)");
   // One-time wait so the plan is usable from any stream afterwards.
@@ -401,12 +463,14 @@ int get_plan(DeviceState& st, int mode, int n, const muon_shape_t* shapes, float
   plan->d_gram = reinterpret_cast<GemmItem*>(dv + o_gram);
   plan->d_poly = reinterpret_cast<GemmItem*>(dv + o_poly);
   plan->d_upd = reinterpret_cast<GemmItem*>(dv + o_upd);
+  plan->d_red = reinterpret_cast<RedItem*>(dv + o_red);
   plan->n_mom = (int)mom.size();
   plan->n_cast = (int)cast.size();
   plan->n_apply = (int)apply.size();
   plan->n_gram = (int)gram.size();
   plan->n_poly = (int)poly.size();
   plan->n_upd = (int)updl.size();
+  plan->n_red = (int)red.size();
   st.plans.push_front(std::move(plan));
   while (st.plans.size() > kMaxPlans) st.plans.pop_back();
   *out = st.plans.front().get();
@@ -462,15 +526,19 @@ int run(int mode, float* const* params, const float* const* grads, float* const*
     const float* ck = coeffs + (size_t)k * stride;  // iteration k's a, b, c
     const float ca = ck[0], cb = ck[1], cc = ck[2];
     rc = timed(MUON_KERNEL_GRAM, stream,
-               [&] { return launch_gemm(GEMM_GRAM, p->d_desc, p->d_gram, p->n_gram, src, ca, cb, cc, stream); },
+               [&] {
+                 const hipError_t e = launch_gemm(GEMM_GRAM, p->d_desc, p->d_gram, p->n_gram, src, ca, cb, cc,
+                                                  p->gram_part, stream);
+                 return e != hipSuccess ? e : launch_gram_reduce(p->d_desc, p->d_red, p->n_red, p->gram_part, stream);
+               },
                "gram kernel launch");
     if (rc) return rc;
     rc = timed(MUON_KERNEL_POLY, stream,
-               [&] { return launch_gemm(GEMM_POLY, p->d_desc, p->d_poly, p->n_poly, src, ca, cb, cc, stream); },
+               [&] { return launch_gemm(GEMM_POLY, p->d_desc, p->d_poly, p->n_poly, src, ca, cb, cc, nullptr, stream); },
                "poly kernel launch");
     if (rc) return rc;
     rc = timed(MUON_KERNEL_UPDATE, stream,
-               [&] { return launch_gemm(GEMM_UPDATE, p->d_desc, p->d_upd, p->n_upd, src, ca, cb, cc, stream); },
+               [&] { return launch_gemm(GEMM_UPDATE, p->d_desc, p->d_upd, p->n_upd, src, ca, cb, cc, nullptr, stream); },
                "update kernel launch");
     if (rc) return rc;
   }

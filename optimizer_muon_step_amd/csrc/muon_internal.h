@@ -53,10 +53,33 @@ struct MatDesc {
   int32_t pad_;
 };
 
-// GEMM work item: one output tile of one matrix.
+// GEMM work item: one output tile of one matrix, or (GRAM only) one K chunk
+// of a tile whose chunks are summed by the reduce pass.
 struct GemmItem {
   int32_t mat;
   int16_t ti, tj;  // tile row / column in units of the launch's tile shape
+  int32_t k0;      // first K slice (units of 64)
+  int32_t kn;      // K slices, 0 = the whole K
+  int32_t slot;    // fp32 partial tile this chunk writes, -1 = none
+};
+
+// Long-K Gram tiles.  When a tile's K is more than twice the per-CU share of
+// a Gram launch (so a few tiles would keep most CUs idle), tiles longer than
+// the share are cut into K chunks of about that share, at least
+// GRAM_SPLIT_MIN slices; each chunk writes an fp32 partial tile and the
+// reduce pass sums a tile's chunks in K order, rounds once to bf16 and
+// mirrors.
+constexpr int GRAM_SPLIT_MIN = 16;  // slices of 64
+constexpr int NS_CUS = 256;         // CUs of the device the split is sized for
+constexpr int RED_TILE = 64;        // reduce pass: 64x64 sub-tile per block
+
+// Reduce work item: one 64x64 sub-tile of a split Gram tile.
+struct RedItem {
+  int32_t mat;
+  int16_t ti, tj;    // Gram tile (units of GRAM_BM)
+  int32_t slot0;     // first partial tile of its chunks
+  int16_t nchunk;    // chunks, summed in order
+  int8_t bi, bj;     // sub-tile within the Gram tile (units of RED_TILE)
 };
 
 // Elementwise work item: chunk (momentum) or tile (cast / apply) of a matrix.
@@ -100,7 +123,9 @@ hipError_t launch_cast(const MatDesc* d, const EwItem* items, int n_items, float
 hipError_t launch_apply(const MatDesc* d, const EwItem* items, int n_items, float lr, int src,
                         int write_w, hipStream_t s);
 hipError_t launch_gemm(int kind, const MatDesc* d, const GemmItem* items, int n_items, int src,
-                       float ca, float cb, float cc, hipStream_t s);
+                       float ca, float cb, float cc, float* part, hipStream_t s);
+hipError_t launch_gram_reduce(const MatDesc* d, const RedItem* items, int n_items, const float* part,
+                              hipStream_t s);
 hipError_t launch_adamw(const AdamDesc* d, const EwItem* items, int n_items, const AdamConst& c, hipStream_t s);
 
 // Source and destination of the three arrays (param, exp_avg, exp_avg_sq)

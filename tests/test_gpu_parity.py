@@ -82,7 +82,7 @@ def _monomial(n, m, rng, transpose):
 
 
 @pytest.mark.parametrize("shape,transpose", [((12, 20), False), ((200, 300), False), ((130, 260), True),
-                                             ((256, 256), False)])
+                                             ((256, 256), False), ((40, 3000), False), ((300, 9000), True)])
 def test_monomial_step_bit_exact(shape, transpose):
     """One non-zero per row and column: every dot product has one term, so the
     GPU must reproduce the oracle's storage points bit for bit."""
@@ -96,6 +96,44 @@ def test_monomial_step_bit_exact(shape, transpose):
     assert np.array_equal(Mg[0].cpu().numpy(), r["buf"])
     assert np.array_equal(bf16_to_np(Ug[0]), r["O"])
     assert np.array_equal(Wg[0].cpu().numpy(), r["W"])
+
+
+# Long-K Gram tiles cut into K chunks whose fp32 partials a reduce pass sums:
+# one diagonal tile (256 x 256 of a 64-row matrix), diagonal and off-diagonal
+# tiles of a 512-row matrix, and a ragged tall one; alone and mixed with
+# matrices whose tiles are not cut.
+@pytest.mark.parametrize("shape", [(64, 4100), (512, 20000), (20001, 300)])
+def test_newton_schulz_long_k_split(shape):
+    import optimizer_muon_step_amd as mu
+    say(f"[ns long K] shape={shape}")
+    bits = _rand_bf16(shape, 31 + shape[0] + shape[1])
+    x = bf16_gpu(bits)
+    out = empty_bf16(shape)
+    mu.muon_newton_schulz([x], [out], 5, COEFFS)
+    X0 = om.bf16_to_f32(bits)
+    Xc, tr = om.canonical(X0)
+    want = om.newton_schulz(np.ascontiguousarray(Xc), 5, COEFFS)
+    want = want.T if tr else want
+    e = rel_f(bf16_to_np(out), want)
+    say(f"  relF {e:.3e}")
+    assert e <= NS_TOL
+
+
+def test_newton_schulz_long_k_mixed_with_short():
+    import optimizer_muon_step_amd as mu
+    shapes = [(512, 20000), (256, 256), (300, 200), (64, 2304)]
+    bits = [_rand_bf16(s, 200 + i) for i, s in enumerate(shapes)]
+    xs = [bf16_gpu(b) for b in bits]
+    outs = [empty_bf16(s) for s in shapes]
+    mu.muon_newton_schulz(xs, outs, 5, COEFFS)
+    for s, b, o in zip(shapes, bits, outs):
+        X0 = om.bf16_to_f32(b)
+        Xc, tr = om.canonical(X0)
+        want = om.newton_schulz(np.ascontiguousarray(Xc), 5, COEFFS)
+        want = want.T if tr else want
+        e = rel_f(bf16_to_np(o), want)
+        say(f"  {s}: relF {e:.3e}")
+        assert e <= NS_TOL
 
 
 def _run_config(name, steps=2, sample=None):
