@@ -211,6 +211,25 @@ def test_workspace_bytes_host_logic(lib):
     assert "shape" in lib.muon_last_error().decode()
 
 
+def test_workspace_bytes_long_k_gram_split(lib):
+    """A Gram tile whose K is more than twice the call's per-CU share is cut
+    into K chunks, one fp32 256x256 partial tile each: the only workspace
+    term that depends on the other matrices of the call."""
+    def ws(shapes):
+        return lib.muon_workspace_bytes(_lib.shape_array(shapes), len(shapes))
+    base = ws([])
+    part = 256 * 256 * 4
+    a = (256, 4096)    # one Gram tile of 64 K slices; alone the share is 16: 4 chunks
+    b = (2048, 2048)   # 36 tiles of 32 slices, never more than twice the share
+    alone = ws([a]) - base
+    b1 = ws([b]) - base
+    # with eight b the share is ceil((64 + 8 * 36 * 32) / 256) = 37: a is not cut
+    assert ws([a] + [b] * 8) - base == (alone - 4 * part) + 8 * b1
+    # with one b the share is ceil((64 + 1152) / 256) = 5 -> 16: a is cut in 4
+    # again, and b's 36 tiles, longer than the share, in 2 each
+    assert ws([a, b]) - base == alone + b1 + 36 * 2 * part
+
+
 def test_timing_enable_validation(lib):
     assert lib.muon_timing_enable(99) == -1
     assert lib.muon_timing_enable(-1) == 0
