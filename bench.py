@@ -169,6 +169,42 @@ def bench_vendor_ns(torch, wl, ns_flops_step, steps=20):
             "ms_per_step": round(ms, 4), "TFLOP/s_algorithmic": round(ns_flops_step / (ms * 1e-3) / 1e12, 1)}
 
 
+def bench_measured_peaks(torch, reps=20):
+    """Measured denominators beside the spec peaks: a large square bf16
+    matmul through torch (hipBLASLt) and a plain 1 GiB device-to-device
+    copy (bytes read plus bytes written per second)."""
+    n = 8192
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(11)
+    a = torch.randn((n, n), generator=gen, device="cuda").to(torch.bfloat16)
+    b = torch.randn((n, n), generator=gen, device="cuda").to(torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    gemm_tf = 2.0 * n ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del a, b
+    src = torch.empty(256 * 1024 * 1024, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2.0 * src.numel() * 4 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    return {"bf16_gemm_TFLOP/s": round(gemm_tf, 1), "bf16_gemm_what": "torch.matmul 8192x8192x8192 bf16 (hipBLASLt)",
+            "copy_GB/s": round(copy_gbs, 1), "copy_what": "1 GiB device-to-device copy, read + write bytes"}
+
+
 def bench_small(torch, mu, wl, steps=200):
     """Small workloads, where launch overhead matters: steps/s of eager calls
     and of the same step captured once into a HIP graph and replayed."""
@@ -276,7 +312,7 @@ def main():
                     help="skip the per-kernel-family timing pass after the timed region")
     ap.add_argument("--no-adamw", action="store_true", help="skip the AdamW measurement after the timed region")
     ap.add_argument("--no-vendor", action="store_true",
-                    help="skip the torch/hipBLASLt Newton-Schulz comparison after the timed region")
+                    help="skip the torch/hipBLASLt comparisons (Newton-Schulz iterations, measured GEMM and copy peaks)")
     ap.add_argument("--no-small", action="store_true",
                     help="skip the small-workload (eager vs graph replay) measurement after the timed region")
     ap.add_argument("--no-large", action="store_true",
@@ -376,6 +412,13 @@ def main():
     small = None if args.no_small else bench_small(torch, mu, wl)
     large = None if args.no_large else bench_large(torch, mu, wl)
     vendor = None if args.no_vendor else bench_vendor_ns(torch, wl, ns_flops_step)
+    peaks = None if args.no_vendor else bench_measured_peaks(torch)
+    if peaks is not None and breakdown is not None:
+        for name, v in breakdown.items():
+            if "TFLOP/s" in v:
+                v["frac_measured_gemm_peak"] = round(v["TFLOP/s"] / peaks["bf16_gemm_TFLOP/s"], 4)
+            elif "GB/s" in v:
+                v["frac_measured_copy"] = round(v["GB/s"] / peaks["copy_GB/s"], 4)
 
     # A plain copy of known size, outside the timed region: it calibrates
     # rocprofv3's FETCH_SIZE / WRITE_SIZE counters when this script is profiled.
@@ -435,6 +478,8 @@ def main():
             vendor["library_ns_ms_per_step"] = breakdown["ns_all"]["ms_per_step"]
             vendor["speedup_of_library"] = round(vendor["ms_per_step"] / breakdown["ns_all"]["ms_per_step"], 2)
         out["vendor_ns_baseline"] = vendor
+    if peaks is not None:
+        out["measured_peaks"] = peaks
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_budget)
     print(json.dumps(out), flush=True)
