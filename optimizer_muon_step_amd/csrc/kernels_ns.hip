@@ -299,10 +299,15 @@ __device__ __forceinline__ void ns_gemm_tile(const MatDesc* __restrict__ descs, 
         acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[nj], af[mi], acc[mi][nj], 0, 0, 0);
   };
 
+  // A diagonal tile keeps only its values on and above the diagonal (the
+  // mirror supplies the rest): a wave whose sub-tile lies strictly below it
+  // multiplies nothing.
+  const bool skip_lower = same_rows && wi * WTM >= wj * WTN + WTN;
   auto compute = [&](int s) {
     const LDS_AS char* st = (const LDS_AS char*)lds + a_off(s);
     const uint32_t st_addr = (uint32_t)(uintptr_t)((const LDS_AS char*)lds + b_off(s));
     if constexpr (!NN) {
+      if (skip_lower) return;
 #pragma unroll
       for (int kk = 0; kk < BK / 16; ++kk) {
         bf16x8 af[TM], bfr[TN];
