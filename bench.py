@@ -63,9 +63,13 @@ def cpu_baseline(budget_s):
     import numpy as np
     from oracle import muon_oracle as om
     from optimizer_muon_step_amd import workloads as wl
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        cores = max(int(i.get("num_threads", 1)) for i in threadpool_info()) if threadpool_info() else 1
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        cores = max(int(i.get("num_threads", 1)) for i in info) if info else 1
+        if info:
+            blas = f"{info[0].get('internal_api')} {info[0].get('version')}"
     except Exception:
         cores = os.cpu_count() or 1
     specs = wl.config_specs(WORKLOAD)
@@ -82,7 +86,7 @@ def cpu_baseline(budget_s):
         if elapsed >= budget_s:
             break
     sec_per_step = elapsed / done * len(layers)
-    return {"value": 1.0 / sec_per_step, "unit": "steps/s", "cores": cores, "kind": "oracle",
+    return {"value": 1.0 / sec_per_step, "unit": "steps/s", "cores": cores, "kind": "oracle", "blas": blas,
             "sample": f"{done} of {len(layers)} layers ({4 * done} of {len(specs)} matrices), one step each, "
                       f"{elapsed:.1f} s, scaled to the full 48-matrix step"}
 
