@@ -1,4 +1,5 @@
-"""Build libmuon.so (the gfx950 HIP kernels and the C ABI) in place with hipcc."""
+"""Build libmuon.so (the gfx950 HIP kernels and the C ABI) in place with
+hipcc, and the plain C caller muon_c_example linked against it."""
 from __future__ import annotations
 
 import os
@@ -10,6 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmuon.so")
+C_EXAMPLE = os.path.join(HERE, "muon_c_example")
 SOURCES = ["muon_api.hip", "kernels_elementwise.hip", "kernels_ns.hip", "kernels_adamw.hip"]
 ARCH = "gfx950"
 
@@ -48,7 +50,27 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
     if verbose and res.stderr.strip():
         sys.stderr.write(res.stderr)
     os.replace(tmp, LIB)
+    build_c_example(verbose)
     return LIB
+
+
+def build_c_example(verbose: bool = False) -> str:
+    """Compile csrc/c_example.c with the host C compiler against libmuon.so."""
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if not cc:
+        raise RuntimeError("no host C compiler")
+    cmd = [cc, "-std=c11", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(rocm, "include"), "-I", os.path.join(ROOT, "include"),
+           os.path.join(CSRC, "c_example.c"), "-L", HERE, "-lmuon", "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN", "-Wl,-rpath," + os.path.join(rocm, "lib"), "-o", C_EXAMPLE]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"{cc} failed with exit code {res.returncode}")
+    return C_EXAMPLE
 
 
 if __name__ == "__main__":
