@@ -1,9 +1,9 @@
-"""Optimizer memory: the "new optimizer" thread (tweet 3/8) says the new optimizer needs half
-of AdamW's optimizer memory.  The state each step carries to the next is one
-fp32 momentum buffer per parameter for Muon (the momentum[] argument of
-muon_step) against two fp32 moments for AdamW (exp_avg[] and exp_avg_sq[] of
-muon_adamw_step).  Pinned by what the oracle steps return and by the byte
-count on the GPT-2-124M hidden set."""
+"""Optimizer memory: the "new optimizer" thread (tweet 3/8) puts the new
+optimizer at half of AdamW's optimizer memory.  The state each step carries
+to the next is one fp32 momentum buffer per parameter for Muon (the
+momentum[] argument of muon_step) against two fp32 moments for AdamW
+(exp_avg[] and exp_avg_sq[] of muon_adamw_step).  Pinned by what the oracle
+steps return and by the byte count on the GPT-2-124M hidden set."""
 import numpy as np
 
 from oracle import adamw_oracle as ao
