@@ -463,24 +463,27 @@ __device__ __forceinline__ void ns_gemm_tile(const MatDesc* __restrict__ descs, 
   }
   // Results are rounded to bf16 and staged in LDS (the pipeline buffers are
   // free now), then written out as whole 16-byte row segments.
-  wait_vm_lgkm0<0>();
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
   bool has_next = false;
   if constexpr (PF) {
+    // Every wave released stage 0 (slice KT-2) at the last step's barrier, so
+    // the next tile's first slice goes out at once; each wave then collects
+    // the a.X values it parked itself.  The barrier below keeps the staged
+    // tile from overwriting stage 1 or the parking space while another wave
+    // still reads them.
     int nidx = idx + gridDim.x;
     while (nidx < n_items && items[nidx].mat < 0) nidx += gridDim.x;
     has_next = nidx < n_items && (KT % 2 == 0);  // stage 0 is free: the last slice sits in stage 1
     if (has_next) issue_first(items[nidx]);
-    // collect the parked a.X values before the staged tile overwrites them
 #pragma unroll
     for (int nj = 0; nj < TN; ++nj)
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) ein[PARK_MI][nj][e4] = *(const LDS_AS u32x2*)park_addr(nj, e4);
-    wait_vm_lgkm0<63>();
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
+    wait_vm_lgkm0<63>();  // LDS only: the prefetch stays in flight
+  } else {
+    wait_vm_lgkm0<0>();
   }
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
   LDS_AS char* E = (LDS_AS char*)lds + E_OFF;
   constexpr int ROWB = BN * 2;          // staged row bytes
   constexpr int RCH = BN / 8;           // 16-byte chunks per staged row
@@ -568,7 +571,9 @@ __device__ __forceinline__ void ns_gemm_tile(const MatDesc* __restrict__ descs, 
     }
   }
   if constexpr (PF) {
-    __syncthreads();  // staged-tile reads finish before the next tile refills the ring
+    // No barrier here: the next tile refills stage 1 and the parking space
+    // only after its first step's barrier, and stage 0 lies outside the
+    // staged tile.
     carry.pre = has_next;
     carry.prev_full = row0 + BM <= row_lim;
   }
