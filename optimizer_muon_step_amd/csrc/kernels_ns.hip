@@ -135,13 +135,13 @@ __device__ __forceinline__ void ns_gemm_tile(const MatDesc* __restrict__ descs, 
   const uint16_t* Aop;
   const uint16_t* Bop;
   MUON_GLOBAL uint16_t* C;
-  int lda, ldb, ldc, K;
+  int lda, ldb, ldc;
   if (KIND == GEMM_GRAM) {
-    Aop = d.X[src]; Bop = Aop; lda = ldb = d.ld_x; K = d.n_pad; C = gptr(d.A); ldc = d.ld_a;
+    Aop = d.X[src]; Bop = Aop; lda = ldb = d.ld_x; C = gptr(d.A); ldc = d.ld_a;
   } else if (KIND == GEMM_POLY) {
-    Aop = d.A; Bop = Aop; lda = ldb = d.ld_a; K = d.m_pad; C = gptr(d.B); ldc = d.ld_a;
+    Aop = d.A; Bop = Aop; lda = ldb = d.ld_a; C = gptr(d.B); ldc = d.ld_a;
   } else {
-    Aop = d.B; lda = d.ld_a; Bop = d.X[src]; ldb = d.ld_x; K = d.m_pad; C = gptr(d.X[src ^ 1]);
+    Aop = d.B; lda = d.ld_a; Bop = d.X[src]; ldb = d.ld_x; C = gptr(d.X[src ^ 1]);
     ldc = d.ld_x;
   }
   // Output rows are rows of Aop.  An UPDATE tile starts at a multiple of
@@ -150,9 +150,9 @@ __device__ __forceinline__ void ns_gemm_tile(const MatDesc* __restrict__ descs, 
   const int row0 = it.ti * ROWU;
   const int col0 = it.tj * BN;  // output columns: rows of Bop (GRAM/POLY), columns of X (UPDATE)
   const int row_lim = d.m_pad;
-  // A Gram K chunk covers slices k0 .. k0+kn-1 of its tile; every other item
-  // the whole K.
-  const int KT = it.kn > 0 ? it.kn : K / BK;
+  // The item walks K slices k0 .. k0+kn-1 (the host stops at the true n or
+  // m, past which the padding is zero; an UPDATE item's count is even).
+  const int KT = it.kn;
   // K is walked in order, slice s = k-range (k0+s)*BK .. +BK-1, by every
   // tile: the row tiles of one UPDATE column block fetch the same X slices at
   // about the same time and share them in L2.
@@ -472,7 +472,7 @@ __device__ __forceinline__ void ns_gemm_tile(const MatDesc* __restrict__ descs, 
     // still reads them.
     int nidx = idx + gridDim.x;
     while (nidx < n_items && items[nidx].mat < 0) nidx += gridDim.x;
-    has_next = nidx < n_items && (KT % 2 == 0);  // stage 0 is free: the last slice sits in stage 1
+    has_next = nidx < n_items;  // stage 0 is free: KT is even, the last slice sits in stage 1
     if (has_next) issue_first(items[nidx]);
 #pragma unroll
     for (int nj = 0; nj < TN; ++nj)

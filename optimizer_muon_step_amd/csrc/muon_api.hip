@@ -97,7 +97,8 @@ struct GramSplit {
   int64_t slots = 0;
 };
 
-int64_t gram_slices(const Geometry& g) { return g.n_pad / 64; }
+// K slices of a Gram tile: the product runs to the true n (the padding is zero).
+int64_t gram_slices(const Geometry& g) { return ((int64_t)g.n + 63) / 64; }
 int64_t gram_tiles(const Geometry& g) {
   const int64_t t = g.m_pad / GRAM_BM;
   return t * (t + 1) / 2;
@@ -386,12 +387,14 @@ int get_plan(DeviceState& st, int mode, int n, const muon_shape_t* shapes, float
   int32_t slot = 0;
   for (int i = 0; i < n; ++i) {
     const int tg = desc[i].m_pad / GRAM_BM, tm = desc[i].m_pad / SYM_BM, tn = desc[i].n_pad / UPD_BN;
-    const int64_t ks = desc[i].n_pad / 64;
+    const int64_t ks = ((int64_t)desc[i].n + 63) / 64;            // Gram K slices
+    const int32_t kp = (int32_t)(((int64_t)desc[i].m + 63) / 64);      // poly K slices
+    const int32_t ku = (int32_t)(2 * (((int64_t)desc[i].m + 127) / 128));  // update: even, see the kernel
     const int64_t nc = gram_chunks(ks, split.chunk);
     for (int ti = 0; ti < tg; ++ti)
       for (int tj = ti; tj < tg; ++tj) {
         if (nc == 1) {
-          gram_seq.push_back({i, (int16_t)ti, (int16_t)tj, 0, 0, -1});
+          gram_seq.push_back({i, (int16_t)ti, (int16_t)tj, 0, (int32_t)ks, -1});
           gram_cost.push_back(ks);
           continue;
         }
@@ -407,16 +410,16 @@ int get_plan(DeviceState& st, int mode, int n, const muon_shape_t* shapes, float
         slot += (int32_t)nc;
       }
     for (int ti = 0; ti < tm; ++ti)
-      for (int tj = ti; tj < tm; ++tj) poly_seq.push_back({i, (int16_t)ti, (int16_t)tj, 0, 0, -1});
+      for (int tj = ti; tj < tm; ++tj) poly_seq.push_back({i, (int16_t)ti, (int16_t)tj, 0, kp, -1});
     for (int tj = 0; tj < tn; ++tj)
       for (int ti = 0; ti < desc[i].m_pad / UPD_ROWU; ti += UPD_BM / UPD_ROWU) {
-        upd_seq.push_back({i, (int16_t)ti, (int16_t)tj, 0, 0, -1});
-        upd_cost.push_back(desc[i].m_pad);
+        upd_seq.push_back({i, (int16_t)ti, (int16_t)tj, 0, ku, -1});
+        upd_cost.push_back(ku);
       }
   }
   if (slot != split.slots) return fail(MUON_EINVAL, "internal: %d Gram partial tiles planned, %lld sized", slot, (long long)split.slots);
   std::vector<int64_t> poly_cost(poly_seq.size());
-  for (size_t k = 0; k < poly_seq.size(); ++k) poly_cost[k] = desc[poly_seq[k].mat].m_pad;
+  for (size_t k = 0; k < poly_seq.size(); ++k) poly_cost[k] = poly_seq[k].kn;
   gram = xcd_interleave(gram_seq, gram_cost);
   poly = xcd_interleave(poly_seq, poly_cost);
   updl = xcd_interleave(upd_seq, upd_cost);

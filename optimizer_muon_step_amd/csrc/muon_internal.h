@@ -59,7 +59,7 @@ struct GemmItem {
   int32_t mat;
   int16_t ti, tj;  // tile row / column in units of the launch's tile shape
   int32_t k0;      // first K slice (units of 64)
-  int32_t kn;      // K slices, 0 = the whole K
+  int32_t kn;      // K slices walked: to the true n (GRAM) or m (POLY, UPDATE; even for UPDATE), or a chunk's
   int32_t slot;    // fp32 partial tile this chunk writes, -1 = none
 };
 
