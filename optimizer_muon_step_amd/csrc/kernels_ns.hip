@@ -302,12 +302,17 @@ __device__ __forceinline__ void ns_gemm_tile(const MatDesc* __restrict__ descs, 
   // A diagonal tile keeps only its values on and above the diagonal (the
   // mirror supplies the rest): a wave whose sub-tile lies strictly below it
   // multiplies nothing.
-  const bool skip_lower = same_rows && wi * WTM >= wj * WTN + WTN;
+  // Likewise a wave whose sub-tile lies wholly in the zero padding past the
+  // true m rows (or m / n columns) keeps its zero accumulators, which are
+  // exactly the padding's values.
+  const int out_cols = NN ? d.n : d.m;
+  const bool skip_wave = (same_rows && wi * WTM >= wj * WTN + WTN) || row0 + wi * WTM >= d.m ||
+                         col0 + wj * WTN >= out_cols;
   auto compute = [&](int s) {
+    if (skip_wave) return;
     const LDS_AS char* st = (const LDS_AS char*)lds + a_off(s);
     const uint32_t st_addr = (uint32_t)(uintptr_t)((const LDS_AS char*)lds + b_off(s));
     if constexpr (!NN) {
-      if (skip_lower) return;
 #pragma unroll
       for (int kk = 0; kk < BK / 16; ++kk) {
         bf16x8 af[TM], bfr[TN];
