@@ -52,8 +52,10 @@ __device__ __forceinline__ float nesterov(float g, float m_new, float beta) {
 // partials in index order, so the result does not depend on scheduling (and no
 // device-scope fence is needed inside the streaming kernel).  All loads of a
 // batch are issued before any store so the whole batch is in flight at once.
-// G and M are streamed with non-temporal loads and stores (no reuse inside
-// the step's hot working set): measured 15% faster than cached accesses.
+// G and M are read with non-temporal loads (measured 15% faster than cached
+// ones).  The new M is stored normally: the cast pass reads it again right
+// after, and part of it is still in the memory-side cache then (cast 136
+// against 149 us, momentum 170 against 168).
 __global__ __launch_bounds__(EW_THREADS) void momentum_kernel(const MatDesc* __restrict__ descs,
                                                               const EwItem* __restrict__ items,
                                                               float beta) {
@@ -81,7 +83,7 @@ __global__ __launch_bounds__(EW_THREADS) void momentum_kernel(const MatDesc* __r
       m[v].y = beta * m[v].y + g[v].y;
       m[v].z = beta * m[v].z + g[v].z;
       m[v].w = beta * m[v].w + g[v].w;
-      __builtin_nontemporal_store(m[v], &m4[v * EW_THREADS + threadIdx.x]);
+      m4[v * EW_THREADS + threadIdx.x] = m[v];
       const float ux = nesterov(g[v].x, m[v].x, beta), uy = nesterov(g[v].y, m[v].y, beta);
       const float uz = nesterov(g[v].z, m[v].z, beta), uw = nesterov(g[v].w, m[v].w, beta);
       ss += (double)ux * ux;
