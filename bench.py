@@ -323,8 +323,8 @@ def main():
                     help="skip the GPT-2-XL-shaped and stress workloads measured after the timed region")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the step shards by whole matrices across ranks, which is not built here)", file=sys.stderr)
+        print(f"bench.py: the step is measured on one GPU; --gpus {args.gpus} is not supported "
+              "(sharding whole matrices across ranks is not implemented)", file=sys.stderr)
         return 2
 
     import numpy as np
