@@ -16,7 +16,6 @@ workload (some layers), scaled to steps/s.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -44,16 +43,16 @@ def ns_flops(shapes):
     return gram, poly, upd
 
 
-def traffic_from_profiles(kernel_file):
+def traffic_from_profiles():
     """HBM bytes per launch of the update GEMM, from committed rocprofv3 counter
-    runs, if they were taken on the current kernel source."""
+    runs, if they were taken on the current kernel sources and build options."""
     path = os.path.join(ROOT, "profiles", "ns_update_c3_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    sha = hashlib.sha256(open(kernel_file, "rb").read()).hexdigest()
-    if rec.get("kernel_source_sha256") != sha:
+    from optimizer_muon_step_amd.build import update_kernel_fingerprint
+    if rec.get("kernel_source_sha256") != update_kernel_fingerprint():
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -432,7 +431,6 @@ def main():
     torch.cuda.synchronize()
     del calib, calib2
 
-    kernel_file = os.path.join(ROOT, "optimizer_muon_step_amd", "csrc", "kernels_ns.hip")
     out = {
         "metric": "Muon steps/s on GPT-2-124M hidden matrices; NS TFLOP/s as % bf16 MFMA peak",
         "value": round(args.steps / wall_s, 3),
@@ -463,7 +461,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(upd_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": traffic_from_profiles(kernel_file),
+            "traffic": traffic_from_profiles(),
             "flops_per_launch": upd_f,
             "ms_per_launch": round(upd_ms, 5),
             "launches": upd_launches,

@@ -1,132 +1,23 @@
-// HBM-bound kernels of the Muon step on gfx950:
-//   momentum  M <- beta M + G ; U = G + beta M ; per-matrix sum of U^2 (fp64)
-//   cast      X0 = bf16(U * s), s = 1 / (||U||_F + 1e-7), canonical (m <= n)
+// Cast and apply passes of the Muon step on gfx950 (HBM-bound):
+//   cast      X0 = bf16(U * s), U = G + beta M (Nesterov look-ahead on the
+//             updated buffer), s = 1 / (||U||_F + 1e-7), canonical (m <= n)
 //             padded layout, transposed through LDS for tall matrices
 //   apply     W <- W - lr * X (transposed back through LDS), optional bf16 copy
-// Momentum convention: SGD with a running sum (the "Momentum" section of
-// "07. Training neural networks" notes PyTorch's form without the (1 - beta)
-// factor); the Nesterov look-ahead and the orthogonalisation order follow the
-// "new optimizer" thread, tweet 5/8.  Every fp32 operation here is one IEEE
-// rounding: the library is built with -ffp-contract=off so no product is fused
-// into a sum.
+// The momentum pass, which produces M and the norm, is in kernels_momentum.hip.
+// The orthogonalisation order follows the "new optimizer" thread, tweet 5/8.
+// Every fp32 operation here is one IEEE rounding: the library is built with
+// -ffp-contract=off so no product is fused into a sum.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
 
 #include "bf16_util.h"
+#include "ew_common.h"
 #include "muon_internal.h"
 
 namespace muon {
 
-namespace {
-
-constexpr int kWaves = EW_THREADS / 64;
-
-// Native vector types: HIP's float4/uint2 classes cannot be assigned through
-// global-address-space pointers.
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-// Fixed-order block sum of one double per thread; the total is valid in thread 0.
-__device__ double block_sum(double v, double* red) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  double s = 0.0;
-  if (threadIdx.x == 0) {
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) s += red[w];
-  }
-  return s;
-}
-
-__device__ __forceinline__ float nesterov(float g, float m_new, float beta) {
-  return g + beta * m_new;
-}
-
-}  // namespace
-
-// One work item = MOM_CHUNK consecutive elements of one matrix; it writes one
-// fp64 partial sum of U^2.  norm_finalize_kernel then reduces each matrix's
-// partials in index order, so the result does not depend on scheduling (and no
-// device-scope fence is needed inside the streaming kernel).  All loads of a
-// batch are issued before any store so the whole batch is in flight at once.
-// G and M are read with non-temporal loads (measured 15% faster than cached
-// ones).  The new M is stored normally: the cast pass reads it again right
-// after, and part of it is still in the memory-side cache then (cast 136
-// against 149 us, momentum 170 against 168).
-__global__ __launch_bounds__(EW_THREADS) void momentum_kernel(const MatDesc* __restrict__ descs,
-                                                              const EwItem* __restrict__ items,
-                                                              float beta) {
-  constexpr int V = MOM_CHUNK / (4 * EW_THREADS);  // float4 per thread
-  __shared__ double red[kWaves];
-  const EwItem it = items[blockIdx.x];
-  const MatDesc& d = descs[it.mat];
-  const int64_t total = (int64_t)d.rows * d.cols;
-  const int64_t base = (int64_t)it.idx * MOM_CHUNK;
-  const int64_t end = min(base + (int64_t)MOM_CHUNK, total);
-  const MUON_GLOBAL float* G = gptr(d.G);
-  MUON_GLOBAL float* M = gptr(d.M);
-  double ss = 0.0;
-  if (d.vec4 && end - base == MOM_CHUNK) {
-    const MUON_GLOBAL f32x4* g4 = reinterpret_cast<const MUON_GLOBAL f32x4*>(G + base);
-    MUON_GLOBAL f32x4* m4 = reinterpret_cast<MUON_GLOBAL f32x4*>(M + base);
-    f32x4 g[V], m[V];
-#pragma unroll
-    for (int v = 0; v < V; ++v) g[v] = __builtin_nontemporal_load(&g4[v * EW_THREADS + threadIdx.x]);
-#pragma unroll
-    for (int v = 0; v < V; ++v) m[v] = __builtin_nontemporal_load(&m4[v * EW_THREADS + threadIdx.x]);
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-      m[v].x = beta * m[v].x + g[v].x;
-      m[v].y = beta * m[v].y + g[v].y;
-      m[v].z = beta * m[v].z + g[v].z;
-      m[v].w = beta * m[v].w + g[v].w;
-      m4[v * EW_THREADS + threadIdx.x] = m[v];
-      const float ux = nesterov(g[v].x, m[v].x, beta), uy = nesterov(g[v].y, m[v].y, beta);
-      const float uz = nesterov(g[v].z, m[v].z, beta), uw = nesterov(g[v].w, m[v].w, beta);
-      ss += (double)ux * ux;
-      ss += (double)uy * uy;
-      ss += (double)uz * uz;
-      ss += (double)uw * uw;
-    }
-  } else {
-    // partial or unaligned chunk: scalar elements, batches of 4V per thread
-    for (int64_t b0 = base; b0 < end; b0 += 4 * V * EW_THREADS) {
-      float g[4 * V], m[4 * V];
-#pragma unroll
-      for (int v = 0; v < 4 * V; ++v) {
-        const int64_t e = b0 + v * EW_THREADS + threadIdx.x;
-        g[v] = e < end ? G[e] : 0.0f;
-        m[v] = e < end ? M[e] : 0.0f;
-      }
-#pragma unroll
-      for (int v = 0; v < 4 * V; ++v) {
-        const int64_t e = b0 + v * EW_THREADS + threadIdx.x;
-        if (e < end) {
-          const float mn = beta * m[v] + g[v];
-          M[e] = mn;
-          const float u = nesterov(g[v], mn, beta);
-          ss += (double)u * u;
-        }
-      }
-    }
-  }
-  ss = block_sum(ss, red);
-  if (threadIdx.x == 0) d.part[it.idx] = ss;
-}
-
-// One block per matrix: s = 1 / (sqrt(sum of partials) + 1e-7), the sum taken
-// in a fixed order.
-__global__ __launch_bounds__(EW_THREADS) void norm_finalize_kernel(const MatDesc* __restrict__ descs) {
-  __shared__ double red[kWaves];
-  const MatDesc& d = descs[blockIdx.x];
-  double v = 0.0;
-  for (int k = threadIdx.x; k < d.part_cnt; k += EW_THREADS) v += d.part[k];
-  v = block_sum(v, red);
-  if (threadIdx.x == 0) *d.scale = (float)(1.0 / (sqrt(v) + 1e-7));
-}
+using namespace ew;
 
 // Value of canonical element (i, j) taken from source element (r, c); zero
 // outside the matrix.
@@ -308,16 +199,6 @@ __global__ __launch_bounds__(EW_THREADS) void apply_kernel(const MatDesc* __rest
         if (c + k < d.cols) U[off + k] = (uint16_t)h[q][k];
     }
   }
-}
-
-hipError_t launch_momentum(const MatDesc* d, const EwItem* items, int n_items, int n_mats, float beta,
-                           hipStream_t s) {
-  if (n_items == 0) return hipSuccess;
-  momentum_kernel<<<n_items, EW_THREADS, 0, s>>>(d, items, beta);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  norm_finalize_kernel<<<n_mats, EW_THREADS, 0, s>>>(d);
-  return hipGetLastError();
 }
 
 hipError_t launch_cast(const MatDesc* d, const EwItem* items, int n_items, float beta, int from_bf16,

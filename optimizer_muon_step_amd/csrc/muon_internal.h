@@ -124,6 +124,8 @@ hipError_t launch_apply(const MatDesc* d, const EwItem* items, int n_items, floa
                         int write_w, hipStream_t s);
 hipError_t launch_gemm(int kind, const MatDesc* d, const GemmItem* items, int n_items, int src,
                        float ca, float cb, float cc, float* part, hipStream_t s);
+hipError_t launch_gemm_gram(const MatDesc* d, const GemmItem* items, int n_items, int src, float* part,
+                            hipStream_t s);
 hipError_t launch_gram_reduce(const MatDesc* d, const RedItem* items, int n_items, const float* part,
                               hipStream_t s);
 hipError_t launch_adamw(const AdamDesc* d, const EwItem* items, int n_items, const AdamConst& c, hipStream_t s);

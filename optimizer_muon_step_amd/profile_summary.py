@@ -22,13 +22,13 @@ from __future__ import annotations
 import argparse
 import collections
 import csv
-import hashlib
 import json
 import os
 import re
 
+from optimizer_muon_step_amd.build import update_kernel_fingerprint
+
 HERE = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SRC = os.path.join(HERE, "csrc", "kernels_ns.hip")
 CALIB_BYTES = 64 * 1024 * 1024 * 4   # bench.py's calibration copy: 64M fp32
 
 FAMILIES = [
@@ -125,7 +125,7 @@ def cmd_traffic(args):
     upd = per.get("ns_update")
     if upd is None:
         raise SystemExit("no update-GEMM dispatch in the counter runs")
-    sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    sha = update_kernel_fingerprint()
     rec = {
         "kernel": "ns_update",
         "kernel_source_sha256": sha,
@@ -148,7 +148,7 @@ def cmd_traffic(args):
         p = per[fam]
         lines.append(f"| {fam} | {p['dispatches']} | {p['fetch_kib_raw']:.0f} | {p['write_kib_raw']:.0f} | "
                      f"{p['fetch_bytes'] / 1e6:.1f} | {p['write_bytes'] / 1e6:.1f} |")
-    lines += ["", f"Kernel source sha256 (kernels_ns.hip): `{sha}`"]
+    lines += ["", f"Update-kernel fingerprint (sha256 of ns_gemm_tile.h, kernels_ns.hip and their build options): `{sha}`"]
     open(args.out_md, "w").write("\n".join(lines) + "\n")
 
 
