@@ -208,6 +208,32 @@ def bench_measured_peaks(torch, reps=20):
             "copy_GB/s": round(copy_gbs, 1), "copy_what": "1 GiB device-to-device copy, read + write bytes"}
 
 
+def family_breakdown(mu, step, shapes, reps=2):
+    """Per-kernel-family time of one step (HIP events around each family's
+    launches, one family per pass of `reps` steps), and from it the NS
+    TFLOP/s (symmetry-aware flops) and the elementwise GB/s (momentum, cast
+    and apply: 12 + 10 + 10 bytes per parameter)."""
+    fam = {}
+    for name, k in (("momentum", mu.KERNEL_MOMENTUM), ("cast", mu.KERNEL_CAST), ("gram", mu.KERNEL_GRAM),
+                    ("poly", mu.KERNEL_POLY), ("update", mu.KERNEL_UPDATE), ("apply", mu.KERNEL_APPLY)):
+        mu.muon_timing_enable(k)
+        for _ in range(reps):
+            step()
+        t, _ = mu.muon_timing_read()
+        mu.muon_timing_enable(-1)
+        fam[name] = t / reps
+    params = sum(r * c for r, c in shapes)
+    ns_ms = fam["gram"] + fam["poly"] + fam["update"]
+    ew_ms = fam["momentum"] + fam["cast"] + fam["apply"]
+    gram_f, poly_f, upd_f = ns_flops(shapes)
+    ns_tf = NS_STEPS * (gram_f + poly_f + upd_f) / (ns_ms * 1e-3) / 1e12
+    ew_gbs = 32.0 * params / (ew_ms * 1e-3) / 1e9
+    return {"ns_ms_per_step": round(ns_ms, 4), "ns_TFLOP/s": round(ns_tf, 1),
+            "ns_frac_bf16_peak": round(ns_tf / PEAK_BF16_TFLOPS, 4),
+            "elementwise_ms_per_step": round(ew_ms, 4), "elementwise_GB/s": round(ew_gbs, 1),
+            "elementwise_frac_hbm_peak": round(ew_gbs / PEAK_HBM_GBS, 4)}
+
+
 def bench_small(torch, mu, wl, steps=200):
     """Small workloads, where launch overhead matters: steps/s of eager calls
     and of the same step captured once into a HIP graph and replayed."""
@@ -242,6 +268,8 @@ def bench_small(torch, mu, wl, steps=200):
         replay = steps / (time.perf_counter() - t0)
         out[name] = {"matrices": len(specs), "params": sum(s.rows * s.cols for s in specs),
                      "eager_steps_per_s": round(eager, 1), "graph_replay_steps_per_s": round(replay, 1)}
+        out[name].update(family_breakdown(mu, lambda: mu.muon_step(W, G, M, LR, BETA, NS_STEPS, COEFFS),
+                                          [(s.rows, s.cols) for s in specs], reps=10))
         del W, G, M, graph
     return out
 
@@ -284,20 +312,9 @@ def bench_large(torch, mu, wl):
         e1.record(stream)
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / steps
-        ns_ms = 0.0
-        for k in (mu.KERNEL_GRAM, mu.KERNEL_POLY, mu.KERNEL_UPDATE):
-            mu.muon_timing_enable(k)
-            for _ in range(2):
-                step()
-            t, cnt = mu.muon_timing_read()
-            mu.muon_timing_enable(-1)
-            ns_ms += t / 2
-        gram_f, poly_f, upd_f = ns_flops(shapes)
-        ns_tf = NS_STEPS * (gram_f + poly_f + upd_f) / (ns_ms * 1e-3) / 1e12
         out[name] = {"matrices": len(specs), "params": sum(r * c for r, c in shapes),
-                     "steps_per_s": round(1e3 / ms, 2), "ms_per_step": round(ms, 4),
-                     "ns_ms_per_step": round(ns_ms, 4), "ns_TFLOP/s": round(ns_tf, 1),
-                     "ns_frac_bf16_peak": round(ns_tf / PEAK_BF16_TFLOPS, 4)}
+                     "steps_per_s": round(1e3 / ms, 2), "ms_per_step": round(ms, 4)}
+        out[name].update(family_breakdown(mu, step, shapes))
         del W, G, M
         torch.cuda.synchronize()
         mu.muon_release()
