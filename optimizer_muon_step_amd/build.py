@@ -38,9 +38,12 @@ FLAGS = [
 # default scheduler, which is faster for them (update 165 against 169 us,
 # momentum 167 against 277 under that strategy).
 _MINREG = ["-mllvm", "-amdgpu-sched-strategy=iterative-minreg"]
+# The AdamW pass takes the iterative ILP strategy: 188.1-188.3 against
+# 190.8-190.9 us per launch on the GPT-2 AdamW set (same box), bit-identical.
 SOURCE_FLAGS = {
     "kernels_ns_gram.hip": _MINREG,
     "kernels_elementwise.hip": _MINREG,
+    "kernels_adamw.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
 }
 
 # Sources of the update GEMM, whose hardware-counter profile is tied to them.
