@@ -9,13 +9,16 @@ synthetic gradients of that shape, resident in HBM before timing starts.
 
 Prints one JSON line.  `roofline` is for the dominant kernel (the Newton-Schulz
 update GEMM X <- aX + BX): algorithmic flops per launch / its mean launch time,
-timed with HIP events on the launch stream inside the timed region.
+timed with HIP events on the launch stream in a pass of the same steps right
+after the timed region (the timed region itself carries only one event per
+step).
 `cpu_baseline` is the CPU oracle timed on a bounded sample of the same
 workload (some layers), scaled to steps/s.
 """
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -367,35 +370,45 @@ def main():
 
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    # The library creates its timing events on first use and reuses them after
-    # each read: one untimed pass with timing on fills the pool, so that no
-    # event is created inside the timed region.
-    mu.muon_timing_enable(mu.KERNEL_UPDATE)
-    for _ in range(args.steps):
-        step()
-    mu.muon_timing_read()
-    mu.muon_timing_enable(-1)
-    torch.cuda.synchronize()
-
-    # Timed region: K steps; the update GEMM's launches are bracketed by HIP
-    # events on this stream.
-    mu.muon_timing_enable(mu.KERNEL_UPDATE)
+    # Per-step HIP events on the launch stream.  torch creates an event's HIP
+    # handle on its first record; recording each one here, before the timed
+    # region, keeps that creation out of it (a first-time creation inside the
+    # region has blocked the host for tens of milliseconds and left the GPU
+    # idle for a step).  The region holds nothing but the steps and these
+    # events: no library instrumentation, no garbage collection.
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    for e in evs:
+        e.record(stream)
     torch.cuda.synchronize()
+    host_t = []
+    gc.disable()
     t0 = time.perf_counter()
     evs[0].record(stream)
     for k in range(args.steps):
         step()
         evs[k + 1].record(stream)
+        host_t.append(time.perf_counter())
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    upd_ms_total, upd_launches = mu.muon_timing_read()
-    mu.muon_timing_enable(-1)
+    gc.enable()
     wall_s = t1 - t0
     ms_per_step = wall_s * 1e3 / args.steps
     ev_ms_per_step = evs[0].elapsed_time(evs[-1]) / args.steps
     step_ms = np.array([evs[k].elapsed_time(evs[k + 1]) for k in range(args.steps)])
+    enq_ms = np.diff(np.array([t0] + host_t)) * 1e3
+
+    # The roofline kernel's launch time, in a pass of its own after the
+    # timed region: the library brackets every update-GEMM launch with HIP
+    # events on the launch stream.  A first pass creates the library's
+    # events; the second is read.
+    roof_steps = max(args.steps, 20)
+    for rep in range(2):
+        mu.muon_timing_enable(mu.KERNEL_UPDATE)
+        for _ in range(roof_steps):
+            step()
+        upd_ms_total, upd_launches = mu.muon_timing_read()
+        mu.muon_timing_enable(-1)
+    torch.cuda.synchronize()
 
     gram_f, poly_f, upd_f = ns_flops(shapes)
     ns_flops_step = NS_STEPS * (gram_f + poly_f + upd_f)
@@ -458,6 +471,8 @@ def main():
         "ms_per_step": round(ms_per_step, 5),
         "ms_per_step_hip_events": round(ev_ms_per_step, 5),
         "step_ms_p10_p50_p90": [round(float(np.percentile(step_ms, q)), 5) for q in (10, 50, 90)],
+        "step_ms_max": round(float(step_ms.max()), 5),
+        "host_enqueue_ms_per_step": [round(float(enq_ms.mean()), 4), round(float(enq_ms.max()), 4)],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -482,6 +497,8 @@ def main():
             "flops_per_launch": upd_f,
             "ms_per_launch": round(upd_ms, 5),
             "launches": upd_launches,
+            "timing": f"HIP events around each update launch on the launch stream, {roof_steps} steps "
+                      "measured after the timed region",
         },
     }
     if breakdown is not None:

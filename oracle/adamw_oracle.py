@@ -52,50 +52,44 @@ DEFAULT_BETAS = (0.9, 0.999)
 DEFAULT_EPS = 1e-8
 
 
-def step_constants(lr, beta1, beta2, eps, step):
-    """Reading W3: the per-call fp32 scalars (emul mode).  Returns a dict."""
-    f32 = np.float32
-    lr32, b1, b2, e32 = f32(lr), f32(beta1), f32(beta2), f32(eps)
+def call_constants(lr, beta1, beta2, eps, weight_decay, step, mode="emul"):
+    """The per-call scalars of one step in the mode's float type (reading W3).
+
+    emul: lr, the betas, eps and lambda are fp32 values; 1 - beta_k and the
+    bias-correction denominators 1 - beta_k^t are evaluated in fp64 from
+    those fp32 values and rounded once to fp32; the decay factor is
+    fp32(1 - fp32(lr * lambda)).  exact: the same quantities in fp64 from the
+    arguments as given."""
     t = int(step)
+    if t < 1:
+        raise ValueError("step counts from 1")
+    T = np.float64 if mode == "exact" else np.float32
+    lr_t, b1, b2, eps_t, lam = (T(x) for x in (lr, beta1, beta2, eps, weight_decay))
     return {
-        "lr": lr32, "beta1": b1, "beta2": b2, "eps": e32,
-        "omb1": f32(1.0 - float(b1)), "omb2": f32(1.0 - float(b2)),
-        "bc1": f32(1.0 - float(b1) ** t), "bc2": f32(1.0 - float(b2) ** t),
+        "T": T, "lr": lr_t, "beta1": b1, "beta2": b2, "eps": eps_t,
+        "omb1": T(1.0 - float(b1)), "omb2": T(1.0 - float(b2)),
+        "bc1": T(1.0 - float(b1) ** t), "bc2": T(1.0 - float(b2) ** t),
+        "decay": T(1.0) - (lr_t * lam),
     }
 
 
 def adamw_step(p, g, u, v, lr, beta1=DEFAULT_BETAS[0], beta2=DEFAULT_BETAS[1], eps=DEFAULT_EPS,
                weight_decay=0.0, step=1, mode="emul"):
-    """One AdamW step on one tensor.  Returns (p_new, u_new, v_new)."""
-    if int(step) < 1:
-        raise ValueError("step counts from 1")
-    if mode == "exact":
-        p = np.asarray(p, np.float64)
-        g = np.asarray(g, np.float64)
-        u = np.asarray(u, np.float64)
-        v = np.asarray(v, np.float64)
-        t = int(step)
-        p = p * (1.0 - lr * weight_decay)
-        u = beta1 * u + (1.0 - beta1) * g
-        v = beta2 * v + (1.0 - beta2) * g * g
-        uh = u / (1.0 - beta1 ** t)
-        vh = v / (1.0 - beta2 ** t)
-        p = p - lr * uh / (np.sqrt(vh) + eps)
-        return p, u, v
-    c = step_constants(lr, beta1, beta2, eps, step)
-    p = np.asarray(p, np.float32)
-    g = np.asarray(g, np.float32)
-    u = np.asarray(u, np.float32)
-    v = np.asarray(v, np.float32)
-    decay = np.float32(1.0) - (c["lr"] * np.float32(weight_decay))
-    p1 = p * decay
-    u1 = (c["beta1"] * u) + (c["omb1"] * g)
-    v1 = (c["beta2"] * v) + ((c["omb2"] * g) * g)
-    uh = u1 / c["bc1"]
-    vh = v1 / c["bc2"]
-    den = np.sqrt(vh) + c["eps"]
-    p2 = p1 - ((c["lr"] * uh) / den)
-    return p2, u1, v1
+    """One AdamW step on one tensor.  Returns (p_new, u_new, v_new).
+
+    Both modes run the same sequence in the mode's float type: the decoupled
+    decay scales theta (W1); the two running means absorb g and g*g; theta
+    then moves against the bias-corrected first mean over the square root of
+    the bias-corrected second mean plus eps.  In emul mode every numpy
+    operation below is one fp32 rounding, in the W4 expression forms."""
+    k = call_constants(lr, beta1, beta2, eps, weight_decay, step, mode)
+    T = k["T"]
+    p, g, u, v = (np.asarray(x, T) for x in (p, g, u, v))
+    p_decayed = p * k["decay"]
+    mean = (k["beta1"] * u) + (k["omb1"] * g)
+    mean_sq = (k["beta2"] * v) + ((k["omb2"] * g) * g)
+    move = (k["lr"] * (mean / k["bc1"])) / (np.sqrt(mean_sq / k["bc2"]) + k["eps"])
+    return p_decayed - move, mean, mean_sq
 
 
 def adamw_multi(params, grads, exp_avg, exp_avg_sq, lr, beta1=DEFAULT_BETAS[0], beta2=DEFAULT_BETAS[1],

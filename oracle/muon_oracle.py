@@ -206,9 +206,3 @@ def muon_step_tensor(W, g, buf, lr, beta, ns_steps, coeffs=DEFAULT_COEFFS, mode=
     m = (shape[0], int(np.prod(shape[1:])))
     r = muon_step_matrix(np.reshape(W, m), np.reshape(g, m), np.reshape(buf, m), lr, beta, ns_steps, coeffs, mode)
     return {k: (np.reshape(v, shape) if k in ("W", "buf", "O", "u") else v) for k, v in r.items()}
-
-
-def muon_step(params, grads, moms, lr, beta, ns_steps, coeffs=DEFAULT_COEFFS, mode="emul"):
-    """One Muon step over a list of matrices (each one independent)."""
-    return [muon_step_matrix(W, g, m, lr, beta, ns_steps, coeffs, mode)
-            for W, g, m in zip(params, grads, moms)]

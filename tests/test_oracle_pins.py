@@ -255,6 +255,39 @@ def test_momentum_step_one_and_two():
     assert rel_f(O, g2 / np.linalg.norm(g2)) > 0.05
 
 
+@pytest.mark.parametrize("mode,beta", [("exact", 0.9), ("exact", 0.95), ("emul", 0.5), ("emul", 0.75)])
+def test_momentum_unrolled_sum_over_steps(mode, beta):
+    """Readings R1 and R2 against their unrolled closed form: from a zero
+    buffer, after k steps buf_k = sum_j beta^(k-j) g_j and the Nesterov vector
+    is u_k = g_k + beta * buf_k.  Exact mode (fp64) must match the sum to
+    rounding; in emul mode beta is a short binary fraction and the gradients
+    small integers, so every intermediate is exact in fp32 and the sum must
+    hold bit for bit.  A look-ahead on the old buffer (u = g + beta * buf_{k-1})
+    or an EMA buffer (beta * buf + (1 - beta) g) fails both."""
+    rng = np.random.default_rng(23)
+    k_steps = 4
+    if mode == "exact":
+        gs = [rng.standard_normal((9, 13)) for _ in range(k_steps)]
+    else:
+        gs = [rng.integers(-8, 9, size=(9, 13)).astype(np.float32) for _ in range(k_steps)]
+    buf = np.zeros_like(gs[0])
+    for k in range(1, k_steps + 1):
+        buf, u = om.nesterov_momentum(gs[k - 1], buf, beta, mode)
+        want_buf = sum(beta ** (k - j) * np.asarray(gs[j - 1], np.float64) for j in range(1, k + 1))
+        want_u = np.asarray(gs[k - 1], np.float64) + beta * want_buf
+        if mode == "exact":
+            assert buf.dtype == np.float64 and u.dtype == np.float64
+            assert np.max(np.abs(buf - want_buf)) <= 1e-13 * np.max(np.abs(want_buf))
+            assert np.max(np.abs(u - want_u)) <= 1e-13 * np.max(np.abs(want_u))
+        else:
+            assert buf.dtype == np.float32 and u.dtype == np.float32
+            assert np.array_equal(buf.astype(np.float64), want_buf)
+            assert np.array_equal(u.astype(np.float64), want_u)
+        if k >= 2:
+            old = want_buf - np.asarray(gs[k - 1], np.float64)  # beta * buf_{k-1}
+            assert np.max(np.abs(u - (np.asarray(gs[k - 1], np.float64) + old))) > 0.1
+
+
 def test_frobenius_scale_eps_reading():
     u = np.array([[3e-7, 4e-7]], np.float32)
     s = om.frobenius_scale(u)
