@@ -32,13 +32,31 @@
  *     not alias one another.  Arrays of pointers and shapes are host arrays,
  *     read only during the call.
  *   - Work is enqueued on `stream` and the call returns without waiting.
- *     Kernel faults surface at the caller's next synchronisation.  Calls that
- *     overlap in time on one device must use the same stream (they share the
- *     library's workspace).
- *   - After the first call with a given set of pointers and shapes (which
- *     builds and caches the plan, and synchronises once), a call only
- *     enqueues kernel launches: no allocation, no copy, no synchronisation,
- *     no memset.  Such calls can be captured into a HIP graph and replayed.
+ *     Kernel faults surface at the caller's next synchronisation.  The
+ *     calls made on one device must be ordered on the GPU: make them on one
+ *     stream, or order the streams yourself (events).  They share the
+ *     library's workspace and plan tables, which each call writes in its
+ *     stream's order.
+ *   - Plans are cached per device and keyed on the shapes (and the entry
+ *     point), not on the pointers.  The first call with a set of shapes
+ *     builds its plan: it allocates the plan's device table block
+ *     (descriptors and work lists, a few hundred KB at most for GPT-2-sized
+ *     sets) and enqueues its upload; it does not synchronise.  A call whose
+ *     pointers differ from the previous call's on that plan enqueues one
+ *     small kernel per 40 matrices that writes them into the descriptors;
+ *     otherwise a call only enqueues the step's kernels.  Up to 8 plans are
+ *     kept; evicting the least recently used one, or growing the library's
+ *     workspace, waits for the device (hipDeviceSynchronize).
+ *   - HIP graph capture: a call made while `stream` is capturing must find
+ *     its plan and a large enough workspace already there (make one call
+ *     with the same shapes first; otherwise it fails with MUON_EINVAL and
+ *     enqueues nothing).  It allocates nothing and records only kernel
+ *     launches: the pointer write and the step.  Its plan, and the workspace
+ *     that plan uses, are then kept until muon_release(): neither eviction
+ *     nor a later, larger call frees them, so the graph can be replayed
+ *     between other calls.  Graphs must not be replayed after
+ *     muon_release(), or after muon_set_workspace() replaced a caller-owned
+ *     workspace they use.
  *   - Arguments are validated on the host before any HIP call; on failure
  *     the call returns a negative code, enqueues nothing and
  *     muon_last_error() describes the problem.
@@ -94,9 +112,7 @@ int muon_step(float* const* params, const float* const* grads, float* const* mom
  * Same as muon_step, and additionally writes the bf16 update X (the value
  * applied as W -= lr * X) to updates[i] (uint16 bf16 bit patterns,
  * rows x cols, caller orientation).  updates may be NULL, or any element may
- * be NULL, to skip that output.  The update pointers are part of the cached
- * plan's key: passing new update buffers every call builds a new plan (with
- * a synchronisation) every call, so reuse them.
+ * be NULL, to skip that output.
  */
 int muon_step_ex(float* const* params, const float* const* grads, float* const* momentum,
                  const muon_shape_t* shapes, int n, float lr, float beta, int ns_steps,
@@ -188,21 +204,34 @@ const char* muon_last_error(void);
 /*
  * Device workspace bytes a call over these shapes needs (bf16 iterates,
  * Gram and polynomial matrices, norm partials, fp32 partial tiles when a
- * long-K Gram product is cut into K chunks, work lists).  Pure host
- * computation.  Returns 0 and sets the error text for invalid shapes.
+ * long-K Gram product is cut into K chunks).  The plan's table block
+ * (descriptors and work lists) is not part of it: each cached plan holds
+ * its own small device allocation.  Pure host computation.  Returns 0 and
+ * sets the error text for invalid shapes.
  */
 size_t muon_workspace_bytes(const muon_shape_t* shapes, int n);
 
 /*
  * Hand the library a caller-owned device workspace for the current device
- * (NULL/0 returns to library-owned workspace).  The caller keeps it alive
- * until muon_release() or another muon_set_workspace() call; calls that need
- * more than `bytes` fail with MUON_ENOMEM.
+ * (NULL/0 returns to library-owned workspace, allocated at the next call).
+ * The caller keeps it alive until muon_release() or another
+ * muon_set_workspace() call; calls that need more than `bytes` fail with
+ * MUON_ENOMEM.  Waits for the device; plans on the previous workspace that
+ * no captured graph uses are dropped.
  */
 int muon_set_workspace(void* dev_ptr, size_t bytes);
 
 /* Free the library's cached workspace and plans on all devices (synchronises). */
 void muon_release(void);
+
+/*
+ * Counters of the current device's plan cache since it was created (or
+ * since muon_release()), for diagnostics: out[0] plans built, out[1] table
+ * uploads, out[2] pointer-write launches, out[3] device synchronisations,
+ * out[4] plans evicted, out[5] workspace allocations.  out is a host array
+ * of 6.  Never touches the device.
+ */
+int muon_plan_stats(int64_t out[6]);
 
 /*
  * Kernel timing for measurement.  muon_timing_enable(k) brackets every

@@ -15,7 +15,7 @@ from . import _lib
 __all__ = [
     "DEFAULT_COEFFS", "MuonError", "matrix_shape", "muon_step", "muon_newton_schulz", "muon_adamw_step", "muon_adamw_untie",
     "muon_workspace_bytes",
-    "muon_set_workspace", "muon_release", "muon_timing_enable", "muon_timing_read", "muon_last_error",
+    "muon_set_workspace", "muon_release", "muon_plan_stats", "muon_timing_enable", "muon_timing_read", "muon_last_error",
     "KERNEL_MOMENTUM", "KERNEL_CAST", "KERNEL_GRAM", "KERNEL_POLY", "KERNEL_UPDATE", "KERNEL_APPLY",
     "KERNEL_ADAMW",
 ]
@@ -235,6 +235,16 @@ def muon_set_workspace(ptr: int | None, nbytes: int = 0) -> None:
 
 def muon_release() -> None:
     _lib.load().muon_release()
+
+
+PLAN_STATS = ("plan_builds", "uploads", "pointer_patches", "device_syncs", "evictions", "workspace_allocs")
+
+
+def muon_plan_stats() -> dict:
+    """Counters of the current device's plan cache (diagnostics)."""
+    arr = (ctypes.c_int64 * 6)()
+    _check(_lib.load().muon_plan_stats(arr))
+    return dict(zip(PLAN_STATS, (int(v) for v in arr)))
 
 
 def muon_timing_enable(kernel: int) -> None:

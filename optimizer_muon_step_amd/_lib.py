@@ -36,6 +36,7 @@ SIGNATURES = {
     "muon_workspace_bytes": (ctypes.c_size_t, [_SHAPES, ctypes.c_int]),
     "muon_set_workspace": (ctypes.c_int, [_P, ctypes.c_size_t]),
     "muon_release": (None, []),
+    "muon_plan_stats": (ctypes.c_int, [ctypes.POINTER(ctypes.c_int64)]),
     "muon_timing_enable": (ctypes.c_int, [ctypes.c_int]),
     "muon_timing_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
 }

@@ -1,0 +1,604 @@
+// Host plan code: validation, canonical geometry, workspace layout, table
+// images and the plan cache.  No GPU calls: device work goes through
+// DeviceOps.  The operation itself is described in include/muon.h.
+#include "plan_host.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+namespace muon {
+
+namespace {
+thread_local std::string g_error;
+int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+}  // namespace
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return code;
+}
+
+const char* last_error_text() { return g_error.c_str(); }
+void clear_error() { g_error.clear(); }
+
+Geometry geometry_of(const muon_shape_t& s) {
+  Geometry g{};
+  g.rows = (int32_t)s.rows;
+  g.cols = (int32_t)s.cols;
+  g.transposed = s.rows > s.cols;
+  g.m = (int32_t)std::min(s.rows, s.cols);
+  g.n = (int32_t)std::max(s.rows, s.cols);
+  g.m_pad = (int32_t)round_up(g.m, NS_PAD_M);
+  g.n_pad = (int32_t)round_up(g.n, NS_PAD_N);
+  g.part_cnt = (int32_t)((s.rows * s.cols + MOM_CHUNK - 1) / MOM_CHUNK);
+  g.ld_x = g.n_pad + NS_LD_PAD;
+  g.ld_a = g.m_pad + NS_LD_PAD;
+  g.x_bytes = align_up((size_t)g.m_pad * g.ld_x * 2);
+  // A and B carry NS_PAD_M spare rows: an update tile may hang over the last
+  // rows and fetch (never store) up to UPD_BM - UPD_ROWU rows past m_pad.
+  static_assert(UPD_BM - UPD_ROWU <= NS_PAD_M, "spare rows");
+  g.a_bytes = align_up((size_t)(g.m_pad + NS_PAD_M) * g.ld_a * 2);
+  g.part_bytes = align_up((size_t)g.part_cnt * sizeof(double));
+  return g;
+}
+
+int check_shapes(const muon_shape_t* shapes, int n) {
+  if (n < 0 || n > MUON_MAX_MATRICES) return fail(MUON_EINVAL, "n = %d outside [0, %d]", n, MUON_MAX_MATRICES);
+  if (n > 0 && !shapes) return fail(MUON_EINVAL, "shapes is NULL");
+  for (int i = 0; i < n; ++i) {
+    const int64_t r = shapes[i].rows, c = shapes[i].cols;
+    if (r < 1 || c < 1) return fail(MUON_EINVAL, "matrix %d: shape %lld x %lld (both must be >= 1)", i, (long long)r, (long long)c);
+    if (r > (int64_t)INT32_MAX || c > (int64_t)INT32_MAX || r * c >= ((int64_t)1 << 31))
+      return fail(MUON_EINVAL, "matrix %d: shape %lld x %lld has 2^31 or more elements", i, (long long)r, (long long)c);
+    const Geometry g = geometry_of(shapes[i]);
+    if ((int64_t)g.m_pad * g.ld_x >= ((int64_t)1 << 31) || (int64_t)(g.m_pad + NS_PAD_M) * g.ld_a >= ((int64_t)1 << 31))
+      return fail(MUON_EINVAL, "matrix %d: padded shape too large", i);
+  }
+  return MUON_OK;
+}
+
+// Coefficients: one {a, b, c} for every iteration (stride 0, always required),
+// or a schedule of ns_steps triples (stride 3; may be NULL when ns_steps = 0).
+int check_coeffs(const float* coeffs, int ns_steps, int stride) {
+  if (ns_steps < 0 || ns_steps > MUON_MAX_NS_STEPS)
+    return fail(MUON_EINVAL, "ns_steps = %d outside [0, %d]", ns_steps, MUON_MAX_NS_STEPS);
+  const int count = stride ? 3 * ns_steps : 3;
+  if (count == 0) return MUON_OK;
+  if (!coeffs) return fail(MUON_EINVAL, "coeffs is NULL");
+  for (int k = 0; k < count; ++k)
+    if (!std::isfinite(coeffs[k])) return fail(MUON_EINVAL, "coeffs[%d] is not finite", k);
+  return MUON_OK;
+}
+
+namespace {
+
+struct Range {
+  uintptr_t lo, hi;
+  int mat;
+  const char* what;
+};
+
+// Every listed array must be disjoint from the others.
+int check_ranges(std::vector<Range>& v) {
+  std::sort(v.begin(), v.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
+  for (size_t k = 1; k < v.size(); ++k)
+    if (v[k].lo < v[k - 1].hi)
+      return fail(MUON_EINVAL, "%s of matrix %d overlaps %s of matrix %d", v[k].what, v[k].mat, v[k - 1].what,
+                  v[k - 1].mat);
+  return MUON_OK;
+}
+
+// Long-K Gram split of a call (GRAM_SPLIT_MIN): the chunk length in K
+// slices, 0 when no tile is cut, and the fp32 partial tiles it needs.
+struct GramSplit {
+  int64_t chunk = 0;
+  int64_t slots = 0;
+};
+
+// K slices of a Gram tile: the product runs to the true n (the padding is zero).
+int64_t gram_slices(const Geometry& g) { return ((int64_t)g.n + 63) / 64; }
+int64_t gram_tiles(const Geometry& g) {
+  const int64_t t = g.m_pad / GRAM_BM;
+  return t * (t + 1) / 2;
+}
+int64_t gram_chunks(int64_t slices, int64_t chunk) { return (chunk && slices > chunk) ? (slices + chunk - 1) / chunk : 1; }
+
+GramSplit gram_split_of(const muon_shape_t* shapes, int n) {
+  GramSplit sp;
+  int64_t total = 0, longest = 0;
+  for (int i = 0; i < n; ++i) {
+    const Geometry g = geometry_of(shapes[i]);
+    total += gram_tiles(g) * gram_slices(g);
+    longest = std::max(longest, gram_slices(g));
+  }
+  const int64_t share = std::max<int64_t>(GRAM_SPLIT_MIN, (total + NS_CUS - 1) / NS_CUS);
+  if (longest <= 2 * share) return sp;
+  sp.chunk = share;
+  for (int i = 0; i < n; ++i) {
+    const Geometry g = geometry_of(shapes[i]);
+    const int64_t nc = gram_chunks(gram_slices(g), sp.chunk);
+    if (nc > 1) sp.slots += gram_tiles(g) * nc;
+  }
+  return sp;
+}
+
+// Workgroup w of a launch runs on XCD w % kXcds, and each XCD has its own L2.
+// Cut the locality-ordered tile sequence into kXcds contiguous runs of about
+// equal cost and interleave them, so that each XCD works through one run and
+// its concurrently resident tiles share operands in that XCD's L2.  Within a
+// run, tiles are dispatched longest first (stable, so tiles of equal cost
+// keep their locality order): the short ones then fill the gaps at the end
+// instead of a long tile starting last.  Runs of unequal length are padded
+// with empty items (mat = -1) that exit at once.
+constexpr int kXcds = 8;
+
+std::vector<GemmItem> xcd_interleave(const std::vector<GemmItem>& seq, const std::vector<int64_t>& cost) {
+  int64_t total = 0;
+  for (int64_t c : cost) total += c;
+  std::vector<std::vector<std::pair<int64_t, GemmItem>>> run(kXcds);
+  int64_t acc = 0;
+  int x = 0;
+  for (size_t k = 0; k < seq.size(); ++k) {
+    while (x < kXcds - 1 && acc >= total * (x + 1) / kXcds) ++x;
+    run[x].push_back({cost[k], seq[k]});
+    acc += cost[k];
+  }
+  size_t len = 0;
+  for (auto& r : run) {
+    std::stable_sort(r.begin(), r.end(), [](const auto& a, const auto& b) { return a.first > b.first; });
+    len = std::max(len, r.size());
+  }
+  std::vector<GemmItem> out(len * kXcds, GemmItem{-1, 0, 0, 0, 0, -1});
+  for (int r = 0; r < kXcds; ++r)
+    for (size_t k = 0; k < run[r].size(); ++k) out[k * kXcds + r] = run[r][k].second;
+  return out;
+}
+
+template <typename T>
+T* carve(char*& cur, size_t count) {
+  T* p = reinterpret_cast<T*>(cur);
+  cur += align_up(count * sizeof(T));
+  return p;
+}
+
+}  // namespace
+
+int validate_step(float* const* params, const float* const* grads, float* const* moms, const muon_shape_t* shapes,
+                  int n, float lr, float beta, int ns_steps, const float* coeffs, int stride, uint16_t* const* upd) {
+  int rc = check_shapes(shapes, n);
+  if (rc) return rc;
+  if (!params || !grads || !moms) return fail(MUON_EINVAL, "params, grads and momentum arrays must not be NULL");
+  if (!std::isfinite(lr)) return fail(MUON_EINVAL, "lr is not finite");
+  if (!std::isfinite(beta) || beta < 0.0f || beta >= 1.0f) return fail(MUON_EINVAL, "beta = %g outside [0, 1)", (double)beta);
+  if ((rc = check_coeffs(coeffs, ns_steps, stride))) return rc;
+  std::vector<Range> r;
+  r.reserve(4 * (size_t)n);
+  for (int i = 0; i < n; ++i) {
+    const size_t fb = (size_t)shapes[i].rows * shapes[i].cols * sizeof(float);
+    const void* ptrs[3] = {params[i], grads[i], moms[i]};
+    const char* names[3] = {"params", "grads", "momentum"};
+    for (int k = 0; k < 3; ++k) {
+      if (!ptrs[k]) return fail(MUON_EINVAL, "%s[%d] is NULL", names[k], i);
+      if ((uintptr_t)ptrs[k] % 4) return fail(MUON_EINVAL, "%s[%d] is not 4-byte aligned", names[k], i);
+      r.push_back({(uintptr_t)ptrs[k], (uintptr_t)ptrs[k] + fb, i, names[k]});
+    }
+    if (upd && upd[i]) {
+      if ((uintptr_t)upd[i] % 2) return fail(MUON_EINVAL, "updates[%d] is not 2-byte aligned", i);
+      r.push_back({(uintptr_t)upd[i], (uintptr_t)upd[i] + fb / 2, i, "updates"});
+    }
+  }
+  return check_ranges(r);
+}
+
+int validate_ns(const uint16_t* const* x, uint16_t* const* out, const muon_shape_t* shapes, int n, int ns_steps,
+                const float* coeffs, int stride) {
+  int rc = check_shapes(shapes, n);
+  if (rc) return rc;
+  if (!x || !out) return fail(MUON_EINVAL, "x and out arrays must not be NULL");
+  if ((rc = check_coeffs(coeffs, ns_steps, stride))) return rc;
+  std::vector<Range> r;
+  for (int i = 0; i < n; ++i) {
+    if (!x[i] || !out[i]) return fail(MUON_EINVAL, "x[%d] or out[%d] is NULL", i, i);
+    if ((uintptr_t)x[i] % 2 || (uintptr_t)out[i] % 2) return fail(MUON_EINVAL, "x[%d] or out[%d] is not 2-byte aligned", i, i);
+    const size_t b = (size_t)shapes[i].rows * shapes[i].cols * 2;
+    r.push_back({(uintptr_t)out[i], (uintptr_t)out[i] + b, i, "out"});
+    if (x[i] != out[i]) r.push_back({(uintptr_t)x[i], (uintptr_t)x[i] + b, i, "x"});
+  }
+  return check_ranges(r);
+}
+
+int validate_adamw(float* const* params, const float* const* grads, float* const* u, float* const* v,
+                   const int64_t* numels, const float* wd, int n, float lr, float beta1, float beta2, float eps,
+                   int64_t step) {
+  if (n < 0 || n > MUON_ADAMW_MAX_TENSORS) return fail(MUON_EINVAL, "n = %d outside [0, %d]", n, MUON_ADAMW_MAX_TENSORS);
+  if (n > 0 && (!params || !grads || !u || !v || !numels))
+    return fail(MUON_EINVAL, "params, grads, exp_avg, exp_avg_sq and numels arrays must not be NULL");
+  if (!std::isfinite(lr)) return fail(MUON_EINVAL, "lr is not finite");
+  if (!std::isfinite(beta1) || beta1 < 0.0f || beta1 >= 1.0f) return fail(MUON_EINVAL, "beta1 = %g outside [0, 1)", (double)beta1);
+  if (!std::isfinite(beta2) || beta2 < 0.0f || beta2 >= 1.0f) return fail(MUON_EINVAL, "beta2 = %g outside [0, 1)", (double)beta2);
+  if (!std::isfinite(eps) || eps < 0.0f) return fail(MUON_EINVAL, "eps = %g is not finite and >= 0", (double)eps);
+  if (step < 1) return fail(MUON_EINVAL, "step = %lld: the first step is 1", (long long)step);
+  std::vector<Range> r;
+  r.reserve(4 * (size_t)n);
+  for (int i = 0; i < n; ++i) {
+    if (numels[i] < 0) return fail(MUON_EINVAL, "numels[%d] = %lld is negative", i, (long long)numels[i]);
+    if (wd && (!std::isfinite(wd[i]) || wd[i] < 0.0f))
+      return fail(MUON_EINVAL, "weight_decay[%d] = %g is not finite and >= 0", i, (double)wd[i]);
+    if (numels[i] == 0) continue;
+    if (numels[i] > (int64_t)1 << 40) return fail(MUON_EINVAL, "numels[%d] = %lld is too large", i, (long long)numels[i]);
+    const size_t fb = (size_t)numels[i] * sizeof(float);
+    const void* ptrs[4] = {params[i], grads[i], u[i], v[i]};
+    const char* names[4] = {"params", "grads", "exp_avg", "exp_avg_sq"};
+    for (int k = 0; k < 4; ++k) {
+      if (!ptrs[k]) return fail(MUON_EINVAL, "%s[%d] is NULL", names[k], i);
+      if ((uintptr_t)ptrs[k] % 4) return fail(MUON_EINVAL, "%s[%d] is not 4-byte aligned", names[k], i);
+      r.push_back({(uintptr_t)ptrs[k], (uintptr_t)ptrs[k] + fb, i, names[k]});
+    }
+  }
+  return check_ranges(r);
+}
+
+int validate_untie(const float* const src[3], float* const dst[3], int64_t rows, int64_t cols, int transpose) {
+  if (rows < 1 || cols < 1) return fail(MUON_EINVAL, "rows = %lld, cols = %lld: both must be >= 1", (long long)rows, (long long)cols);
+  if (rows > ((int64_t)1 << 40) / cols) return fail(MUON_EINVAL, "rows * cols above 2^40");
+  if (transpose != 0 && transpose != 1) return fail(MUON_EINVAL, "transpose = %d is neither 0 nor 1", transpose);
+  const char* sn[3] = {"param", "exp_avg", "exp_avg_sq"};
+  const char* dn[3] = {"new_param", "new_exp_avg", "new_exp_avg_sq"};
+  const size_t b = (size_t)rows * cols * sizeof(float);
+  std::vector<Range> r;
+  for (int k = 0; k < 3; ++k) {
+    if (!src[k] || !dst[k]) return fail(MUON_EINVAL, "%s or %s is NULL", sn[k], dn[k]);
+    if ((uintptr_t)src[k] % 4 || (uintptr_t)dst[k] % 4) return fail(MUON_EINVAL, "%s or %s is not 4-byte aligned", sn[k], dn[k]);
+    r.push_back({(uintptr_t)dst[k], (uintptr_t)dst[k] + b, 0, dn[k]});
+  }
+  const int rc = check_ranges(r);
+  if (rc) return rc;
+  // sources may share memory with one another (read only), never with a destination
+  for (int k = 0; k < 3; ++k)
+    for (int j = 0; j < 3; ++j)
+      if ((uintptr_t)src[k] < (uintptr_t)dst[j] + b && (uintptr_t)dst[j] < (uintptr_t)src[k] + b)
+        return fail(MUON_EINVAL, "%s overlaps %s", sn[k], dn[j]);
+  return MUON_OK;
+}
+
+size_t workspace_bytes_of(const muon_shape_t* shapes, int n) {
+  size_t total = kControlBytes;
+  for (int i = 0; i < n; ++i) {
+    const Geometry g = geometry_of(shapes[i]);
+    total += 2 * g.x_bytes + 2 * g.a_bytes + g.part_bytes;
+  }
+  total += align_up((size_t)gram_split_of(shapes, n).slots * GRAM_BM * GRAM_BM * sizeof(float));
+  return total;
+}
+
+int build_tables(int mode, const muon_shape_t* shapes, int n, char* ws_base, PlanTables* out) {
+  PlanTables& T = *out;
+  std::vector<MatDesc> desc(n);
+  std::vector<EwItem> mom, cast, apply;
+  char* cur = ws_base;
+  float* scales = reinterpret_cast<float*>(cur);
+  cur += kControlBytes;
+  for (int i = 0; i < n; ++i) {
+    const Geometry g = geometry_of(shapes[i]);
+    MatDesc& d = desc[i];
+    memset(&d, 0, sizeof d);
+    d.X[0] = carve<uint16_t>(cur, g.x_bytes / 2);
+    d.X[1] = carve<uint16_t>(cur, g.x_bytes / 2);
+    d.A = carve<uint16_t>(cur, g.a_bytes / 2);
+    d.B = carve<uint16_t>(cur, g.a_bytes / 2);
+    d.part = carve<double>(cur, g.part_bytes / sizeof(double));
+    d.scale = scales + i;
+    d.rows = g.rows;
+    d.cols = g.cols;
+    d.m = g.m;
+    d.n = g.n;
+    d.m_pad = g.m_pad;
+    d.n_pad = g.n_pad;
+    d.ld_x = g.ld_x;
+    d.ld_a = g.ld_a;
+    d.transposed = g.transposed;
+    d.part_cnt = g.part_cnt;
+    if (mode == MODE_STEP)
+      for (int c = 0; c < g.part_cnt; ++c) mom.push_back({i, c});
+    const int ct = (g.m_pad / CAST_TILE) * (g.n_pad / CAST_TILE);
+    for (int t = 0; t < ct; ++t) cast.push_back({i, t});
+    const int at = ((g.rows + CAST_TILE - 1) / CAST_TILE) * ((g.cols + CAST_TILE - 1) / CAST_TILE);
+    for (int t = 0; t < at; ++t) apply.push_back({i, t});
+  }
+  // The cast re-reads what the momentum pass just streamed: walking it
+  // backwards starts with the lines most likely still in the memory-side
+  // cache.
+  std::reverse(cast.begin(), cast.end());
+  // Partial tiles of split Gram tiles follow the matrices' buffers.
+  const GramSplit split = gram_split_of(shapes, n);
+  T.gram_part_off = (size_t)(cur - ws_base);
+  (void)carve<float>(cur, (size_t)split.slots * GRAM_BM * GRAM_BM);
+  // GEMM tiles.  Per matrix in an order that reuses operands (update: all row
+  // tiles of one column block in a row, sharing that block of X; symmetric
+  // phases: upper-triangle tiles row by row), then spread over the XCDs.
+  // Gram and poly tiles differ in size (256 and 128); a long-K Gram tile may
+  // be cut into K chunks, each its own item, summed by the reduce pass.
+  std::vector<GemmItem> gram_seq, poly_seq, upd_seq;
+  std::vector<RedItem> red;
+  std::vector<int64_t> gram_cost, upd_cost;
+  int32_t slot = 0;
+  for (int i = 0; i < n; ++i) {
+    const int tg = desc[i].m_pad / GRAM_BM, tm = desc[i].m_pad / SYM_BM, tn = desc[i].n_pad / UPD_BN;
+    const int64_t ks = ((int64_t)desc[i].n + 63) / 64;                   // Gram K slices
+    const int32_t kp = (int32_t)(((int64_t)desc[i].m + 63) / 64);          // poly K slices
+    const int32_t ku = (int32_t)(2 * (((int64_t)desc[i].m + 127) / 128));  // update: even, see the kernel
+    const int64_t nc = gram_chunks(ks, split.chunk);
+    for (int ti = 0; ti < tg; ++ti)
+      for (int tj = ti; tj < tg; ++tj) {
+        if (nc == 1) {
+          gram_seq.push_back({i, (int16_t)ti, (int16_t)tj, 0, (int32_t)ks, -1});
+          gram_cost.push_back(ks);
+          continue;
+        }
+        for (int64_t c = 0; c < nc; ++c) {
+          const int64_t a = ks * c / nc, b = ks * (c + 1) / nc;
+          gram_seq.push_back({i, (int16_t)ti, (int16_t)tj, (int32_t)a, (int32_t)(b - a), slot + (int32_t)c});
+          gram_cost.push_back(b - a);
+        }
+        constexpr int SUB = GRAM_BM / RED_TILE;
+        for (int bi = 0; bi < SUB; ++bi)
+          for (int bj = 0; bj < SUB; ++bj)
+            if (ti != tj || bi <= bj) red.push_back({i, (int16_t)ti, (int16_t)tj, slot, (int16_t)nc, (int8_t)bi, (int8_t)bj});
+        slot += (int32_t)nc;
+      }
+    for (int ti = 0; ti < tm; ++ti)
+      for (int tj = ti; tj < tm; ++tj) poly_seq.push_back({i, (int16_t)ti, (int16_t)tj, 0, kp, -1});
+    for (int tj = 0; tj < tn; ++tj)
+      for (int ti = 0; ti < desc[i].m_pad / UPD_ROWU; ti += UPD_BM / UPD_ROWU) {
+        upd_seq.push_back({i, (int16_t)ti, (int16_t)tj, 0, ku, -1});
+        upd_cost.push_back(ku);
+      }
+  }
+  if (slot != split.slots)
+    return fail(MUON_EINVAL, "internal: %d Gram partial tiles planned, %lld sized", slot, (long long)split.slots);
+  std::vector<int64_t> poly_cost(poly_seq.size());
+  for (size_t k = 0; k < poly_seq.size(); ++k) poly_cost[k] = poly_seq[k].kn;
+  const std::vector<GemmItem> gram = xcd_interleave(gram_seq, gram_cost);
+  const std::vector<GemmItem> poly = xcd_interleave(poly_seq, poly_cost);
+  const std::vector<GemmItem> updl = xcd_interleave(upd_seq, upd_cost);
+  const size_t lists = mom.size() + cast.size() + apply.size() + gram.size() + poly.size() + updl.size() + red.size();
+  if (lists > (size_t)INT32_MAX / 2) return fail(MUON_EINVAL, "call of %zu work items is too large", lists);
+
+  size_t off = 0;
+  auto place = [&](size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  T.o_desc = place(sizeof(MatDesc) * n);
+  T.o_mom = place(sizeof(EwItem) * mom.size());
+  T.o_cast = place(sizeof(EwItem) * cast.size());
+  T.o_apply = place(sizeof(EwItem) * apply.size());
+  T.o_gram = place(sizeof(GemmItem) * gram.size());
+  T.o_poly = place(sizeof(GemmItem) * poly.size());
+  T.o_upd = place(sizeof(GemmItem) * updl.size());
+  T.o_red = place(sizeof(RedItem) * red.size());
+  T.image.assign(std::max<size_t>(off, kAlign), 0);
+  char* h = T.image.data();
+  auto put = [&](size_t o, const void* src, size_t bytes) {
+    if (bytes) memcpy(h + o, src, bytes);
+  };
+  put(T.o_desc, desc.data(), sizeof(MatDesc) * n);
+  put(T.o_mom, mom.data(), sizeof(EwItem) * mom.size());
+  put(T.o_cast, cast.data(), sizeof(EwItem) * cast.size());
+  put(T.o_apply, apply.data(), sizeof(EwItem) * apply.size());
+  put(T.o_gram, gram.data(), sizeof(GemmItem) * gram.size());
+  put(T.o_poly, poly.data(), sizeof(GemmItem) * poly.size());
+  put(T.o_upd, updl.data(), sizeof(GemmItem) * updl.size());
+  put(T.o_red, red.data(), sizeof(RedItem) * red.size());
+  T.n_mat = n;
+  T.n_mom = (int)mom.size();
+  T.n_cast = (int)cast.size();
+  T.n_apply = (int)apply.size();
+  T.n_gram = (int)gram.size();
+  T.n_poly = (int)poly.size();
+  T.n_upd = (int)updl.size();
+  T.n_red = (int)red.size();
+  return MUON_OK;
+}
+
+void make_ptr_records(int mode, const muon_shape_t* shapes, int n, float* const* params, const float* const* grads,
+                      float* const* moms, uint16_t* const* upd, const uint16_t* const* xin,
+                      std::vector<PtrRecord>* out) {
+  out->assign(n, PtrRecord{});
+  for (int i = 0; i < n; ++i) {
+    PtrRecord& r = (*out)[i];
+    r.mat = i;
+    r.W = params ? params[i] : nullptr;
+    r.G = grads ? grads[i] : nullptr;
+    r.M = moms ? moms[i] : nullptr;
+    r.upd = upd ? upd[i] : nullptr;
+    r.xin = xin ? xin[i] : nullptr;
+    const bool cols4 = shapes[i].cols % 4 == 0;
+    if (mode == MODE_STEP)
+      r.vec4 = cols4 && (uintptr_t)r.W % 16 == 0 && (uintptr_t)r.G % 16 == 0 && (uintptr_t)r.M % 16 == 0;
+    else
+      r.vec4 = cols4 && (uintptr_t)r.xin % 8 == 0;
+  }
+}
+
+bool same_records(const std::vector<PtrRecord>& a, const std::vector<PtrRecord>& b) {
+  if (a.size() != b.size()) return false;
+  for (size_t i = 0; i < a.size(); ++i)
+    if (a[i].W != b[i].W || a[i].G != b[i].G || a[i].M != b[i].M || a[i].upd != b[i].upd || a[i].xin != b[i].xin ||
+        a[i].vec4 != b[i].vec4 || a[i].mat != b[i].mat)
+      return false;
+  return true;
+}
+
+// ---------------------------------------------------------------- cache ----
+
+PlanCache::~PlanCache() { release_all(); }
+
+void PlanCache::free_plan(Plan* p) {
+  if (p->dev || p->host) ops_->free_tables(p->dev, p->host);
+  p->dev = p->host = nullptr;
+}
+
+void PlanCache::release_all() {
+  for (auto& p : plans_) free_plan(p.get());
+  plans_.clear();
+  for (void* w : retired_) ops_->free_workspace(w);
+  retired_.clear();
+  if (ws_ && ws_owned_) ops_->free_workspace(ws_);
+  ws_ = nullptr;
+  ws_bytes_ = 0;
+  ws_owned_ = false;
+}
+
+// Free every uncaptured plan on workspace ws (the device is idle).
+void PlanCache::drop_uncaptured_on(char* ws) {
+  for (auto it = plans_.begin(); it != plans_.end();) {
+    if ((*it)->ws == ws && !(*it)->captured) {
+      free_plan(it->get());
+      it = plans_.erase(it);
+    } else {
+      ++it;
+    }
+  }
+}
+
+int PlanCache::acquire_workspace(size_t need, bool capturing) {
+  if (ws_ && ws_bytes_ >= need) return MUON_OK;
+  if (ws_ && !ws_owned_)
+    return fail(MUON_ENOMEM, "caller workspace has %zu bytes, this call needs %zu", ws_bytes_, need);
+  if (capturing)
+    return fail(MUON_EINVAL, "this call needs a %zu-byte workspace (%zu now): make one call with these shapes "
+                "before capturing it into a graph", need, ws_bytes_);
+  if (ws_) {
+    // Growing: wait for work that may still use the old buffer.  Plans that
+    // a captured graph uses keep it (retired, freed at release).
+    int rc = ops_->sync_device();
+    ++stats.syncs;
+    if (rc) return rc;
+    drop_uncaptured_on(ws_);
+    bool held = false;
+    for (auto& p : plans_) held = held || p->ws == ws_;
+    if (held)
+      retired_.push_back(ws_);
+    else
+      ops_->free_workspace(ws_);
+    ws_ = nullptr;
+    ws_bytes_ = 0;
+  }
+  void* p = nullptr;
+  const int rc = ops_->alloc_workspace(need, &p);
+  if (rc) return rc;
+  ++stats.ws_allocs;
+  ws_ = static_cast<char*>(p);
+  ws_bytes_ = need;
+  ws_owned_ = true;
+  return MUON_OK;
+}
+
+int PlanCache::set_workspace(void* p, size_t bytes) {
+  const int rc = ops_->sync_device();
+  ++stats.syncs;
+  if (rc) return rc;
+  if (ws_) {
+    drop_uncaptured_on(ws_);
+    bool held = false;
+    for (auto& q : plans_) held = held || q->ws == ws_;
+    if (ws_owned_) {
+      if (held)
+        retired_.push_back(ws_);
+      else
+        ops_->free_workspace(ws_);
+    }
+  }
+  ws_ = static_cast<char*>(p);
+  ws_bytes_ = p ? bytes : 0;
+  ws_owned_ = false;
+  return MUON_OK;
+}
+
+int PlanCache::prepare(int mode, const muon_shape_t* shapes, int n, const std::vector<PtrRecord>& recs,
+                       bool capturing, Plan** out) {
+  int rc = acquire_workspace(workspace_bytes_of(shapes, n), capturing);
+  if (rc) return rc;
+  std::vector<int64_t> key;
+  key.reserve(3 + 2 * (size_t)n);
+  key.push_back(mode);
+  key.push_back(n);
+  key.push_back((int64_t)(uintptr_t)ws_);
+  for (int i = 0; i < n; ++i) {
+    key.push_back(shapes[i].rows);
+    key.push_back(shapes[i].cols);
+  }
+  Plan* plan = nullptr;
+  for (auto it = plans_.begin(); it != plans_.end(); ++it) {
+    if ((*it)->key == key) {
+      if (it != plans_.begin()) plans_.splice(plans_.begin(), plans_, it);
+      plan = plans_.front().get();
+      break;
+    }
+  }
+  if (!plan) {
+    if (capturing)
+      return fail(MUON_EINVAL, "no plan for these shapes yet: make one call with them before capturing it into a graph");
+    auto p = std::make_unique<Plan>();
+    p->key = std::move(key);
+    p->ws = ws_;
+    if ((rc = build_tables(mode, shapes, n, ws_, &p->t))) return rc;
+    if ((rc = ops_->alloc_tables(p->t.image.size(), &p->dev, &p->host))) return rc;
+    if ((rc = ops_->upload(p->dev, p->host, p->t.image.data(), p->t.image.size()))) {
+      free_plan(p.get());
+      return rc;
+    }
+    ++stats.plan_builds;
+    ++stats.uploads;
+    plans_.push_front(std::move(p));
+    plan = plans_.front().get();
+    // Keep at most kMaxPlans uncaptured plans; the least recently used goes
+    // once the device is done with it.
+    size_t uncaptured = 0;
+    for (auto& q : plans_) uncaptured += q->captured ? 0 : 1;
+    if (uncaptured > kMaxPlans) {
+      for (auto it = std::prev(plans_.end());; --it) {
+        if (!(*it)->captured && it->get() != plan) {
+          rc = ops_->sync_device();
+          ++stats.syncs;
+          if (rc) return rc;
+          free_plan(it->get());
+          plans_.erase(it);
+          ++stats.evictions;
+          break;
+        }
+        if (it == plans_.begin()) break;
+      }
+    }
+  }
+  if (capturing) plan->captured = true;
+  // Patch the caller pointers unless the descriptors already hold exactly
+  // these (known only for plans no graph writes into).
+  if (capturing || plan->captured || !plan->ptrs_known || !same_records(plan->ptrs, recs)) {
+    if (!capturing) plan->ptrs_known = false;
+    for (int i = 0; i < n; i += PATCH_MAX) {
+      const int cnt = std::min(PATCH_MAX, n - i);
+      if ((rc = ops_->patch(plan->at<char>(plan->t.o_desc), recs.data() + i, cnt))) return rc;
+      ++stats.patch_calls;
+    }
+    if (!capturing) {
+      plan->ptrs = recs;
+      plan->ptrs_known = true;
+    }
+  }
+  *out = plan;
+  return MUON_OK;
+}
+
+}  // namespace muon
