@@ -13,7 +13,7 @@ import ctypes
 from . import _lib
 
 __all__ = [
-    "DEFAULT_COEFFS", "MuonError", "matrix_shape", "muon_step", "muon_newton_schulz", "muon_adamw_step", "muon_adamw_untie",
+    "DEFAULT_COEFFS", "MuonError", "matrix_shape", "muon_step", "muon_step_noalloc", "muon_newton_schulz", "muon_adamw_step", "muon_adamw_untie",
     "muon_workspace_bytes",
     "muon_set_workspace", "muon_release", "muon_plan_stats", "muon_timing_enable", "muon_timing_read", "muon_last_error",
     "KERNEL_MOMENTUM", "KERNEL_CAST", "KERNEL_GRAM", "KERNEL_POLY", "KERNEL_UPDATE", "KERNEL_APPLY",
@@ -138,6 +138,31 @@ def muon_step(params, grads, momentum, lr=0.02, beta=0.95, ns_steps=5, coeffs=DE
         U = _lib.ptr_array(ptrs)
         entry = lib.muon_step_sched if sched else lib.muon_step_ex
         rc = entry(P, G, M, S, n, float(lr), float(beta), int(ns_steps), C, U, st)
+    _check(rc)
+
+
+def muon_step_noalloc(params, grads, momentum, lr=0.02, beta=0.95, ns_steps=5, coeffs=DEFAULT_COEFFS,
+                      stream=None) -> None:
+    """muon_step for callers that cannot allocate device memory: workspace and
+    tables in the library's static scratch array (MUON_NOALLOC_SCRATCH_BYTES
+    per device); one fixed (a, b, c) triple."""
+    n = len(params)
+    if len(grads) != n or len(momentum) != n:
+        raise ValueError("params, grads and momentum must have the same length")
+    shapes = []
+    for i, (p, g, m) in enumerate(zip(params, grads, momentum)):
+        _fp32_matrix(p, f"params[{i}]"), _fp32_matrix(g, f"grads[{i}]"), _fp32_matrix(m, f"momentum[{i}]")
+        if g.shape != p.shape or m.shape != p.shape:
+            raise ValueError(f"matrix {i}: shapes differ")
+        shapes.append(matrix_shape(p.shape))
+    sched, C = _coeff_arg(coeffs, ns_steps)
+    if sched:
+        raise ValueError("muon_step_noalloc takes one (a, b, c) triple")
+    rc = _lib.load().muon_step_noalloc(_lib.ptr_array([p.data_ptr() for p in params]),
+                                       _lib.ptr_array([g.data_ptr() for g in grads]),
+                                       _lib.ptr_array([m.data_ptr() for m in momentum]), _lib.shape_array(shapes), n,
+                                       float(lr), float(beta), int(ns_steps), C,
+                                       ctypes.c_void_p(_stream_handle(stream)))
     _check(rc)
 
 

@@ -24,6 +24,8 @@ SIGNATURES = {
                                  ctypes.c_int, _FLOAT3, _P]),
     "muon_step_ex": (ctypes.c_int, [_PP, _PP, _PP, _SHAPES, ctypes.c_int, ctypes.c_float, ctypes.c_float,
                                     ctypes.c_int, _FLOAT3, _PP, _P]),
+    "muon_step_noalloc": (ctypes.c_int, [_PP, _PP, _PP, _SHAPES, ctypes.c_int, ctypes.c_float, ctypes.c_float,
+                                         ctypes.c_int, _FLOAT3, _P]),
     "muon_step_sched": (ctypes.c_int, [_PP, _PP, _PP, _SHAPES, ctypes.c_int, ctypes.c_float, ctypes.c_float,
                                        ctypes.c_int, _FLOAT3, _PP, _P]),
     "muon_newton_schulz": (ctypes.c_int, [_PP, _PP, _SHAPES, ctypes.c_int, ctypes.c_int, _FLOAT3, _P]),
