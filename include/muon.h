@@ -256,6 +256,20 @@ void muon_release(void);
 int muon_plan_stats(int64_t out[6]);
 
 /*
+ * Concurrency of one call (1 .. 4, default 1; the setting is process-wide).
+ * Matrices of one canonical shape (m x n, m <= n) form a group; with more
+ * than one lane the groups are spread over up to `lanes` lanes, and each
+ * lane runs its matrices' whole step on an internal stream of the library,
+ * forked from the caller's stream (after everything enqueued there before the
+ * call) and joined back to it, so that one group's kernels fill the GPU while
+ * another's tail off.  1 keeps every kernel on the caller's stream.  Results
+ * are bit-identical for any setting; under graph capture the lanes run one
+ * after another on the capturing stream.  Kernel timing (below) brackets
+ * each lane's launches on that lane's stream.
+ */
+int muon_set_lanes(int lanes);
+
+/*
  * Kernel timing for measurement.  muon_timing_enable(k) brackets every
  * subsequent launch of kernel family k with HIP events on the launch stream;
  * k = -1 stops.  muon_timing_read waits for the recorded events and returns

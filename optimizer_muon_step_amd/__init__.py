@@ -15,7 +15,7 @@ from . import _lib
 __all__ = [
     "DEFAULT_COEFFS", "MuonError", "matrix_shape", "muon_step", "muon_step_noalloc", "muon_newton_schulz", "muon_adamw_step", "muon_adamw_untie",
     "muon_workspace_bytes",
-    "muon_set_workspace", "muon_release", "muon_plan_stats", "muon_timing_enable", "muon_timing_read", "muon_last_error",
+    "muon_set_workspace", "muon_release", "muon_plan_stats", "muon_set_lanes", "muon_timing_enable", "muon_timing_read", "muon_last_error",
     "KERNEL_MOMENTUM", "KERNEL_CAST", "KERNEL_GRAM", "KERNEL_POLY", "KERNEL_UPDATE", "KERNEL_APPLY",
     "KERNEL_ADAMW",
 ]
@@ -270,6 +270,12 @@ def muon_plan_stats() -> dict:
     arr = (ctypes.c_int64 * 6)()
     _check(_lib.load().muon_plan_stats(arr))
     return dict(zip(PLAN_STATS, (int(v) for v in arr)))
+
+
+def muon_set_lanes(lanes: int) -> None:
+    """Concurrency of a call: up to `lanes` shape groups run at once on the
+    library's internal streams (1 = everything on the caller's stream)."""
+    _check(_lib.load().muon_set_lanes(int(lanes)))
 
 
 def muon_timing_enable(kernel: int) -> None:

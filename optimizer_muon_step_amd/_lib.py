@@ -39,6 +39,7 @@ SIGNATURES = {
     "muon_set_workspace": (ctypes.c_int, [_P, ctypes.c_size_t]),
     "muon_release": (None, []),
     "muon_plan_stats": (ctypes.c_int, [ctypes.POINTER(ctypes.c_int64)]),
+    "muon_set_lanes": (ctypes.c_int, [ctypes.c_int]),
     "muon_timing_enable": (ctypes.c_int, [ctypes.c_int]),
     "muon_timing_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
 }

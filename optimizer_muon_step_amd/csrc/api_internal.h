@@ -19,22 +19,23 @@ int capture_status(hipStream_t stream, bool* capturing);
 // Serialises every entry point's use of the library's host state.
 std::mutex& api_mutex();
 
-// Device addresses of one plan's tables (a table block laid out as t says,
+// Device addresses of one lane's tables (a table block laid out as t says,
 // over the workspace ws).
 struct Tables {
   MatDesc* desc;
+  int32_t* mats;
   EwItem *mom, *cast, *apply;
   GemmItem *gram, *poly, *upd;
   RedItem* red;
   float* gram_part;
-  const PlanTables* t;
+  const LaneTables* t;
 };
-Tables tables_at(char* block, const PlanTables& t, char* ws);
+Tables tables_at(char* block, const PlanTables& t, int lane, char* ws);
 
 // Pointer records into the descriptors at desc, PATCH_MAX per launch.
 int patch_records(MatDesc* desc, const std::vector<PtrRecord>& recs, hipStream_t stream);
 
-// The kernel sequence of one call (the caller holds api_mutex()).
+// The kernel sequence of one lane of a call (the caller holds api_mutex()).
 int launch_sequence(int mode, const Tables& v, float lr, float beta, int ns_steps, const float* coeffs, int stride,
                     hipStream_t stream);
 

@@ -107,24 +107,25 @@ __global__ __launch_bounds__(EW_THREADS) void momentum_kernel(const MatDesc* __r
   if (threadIdx.x == 0) d.part[it.idx] = ss;
 }
 
-// One block per matrix: s = 1 / (sqrt(sum of partials) + 1e-7), the sum taken
-// in a fixed order.
-__global__ __launch_bounds__(EW_THREADS) void norm_finalize_kernel(const MatDesc* __restrict__ descs) {
+// One block per matrix of the list: s = 1 / (sqrt(sum of partials) + 1e-7),
+// the sum taken in a fixed order.
+__global__ __launch_bounds__(EW_THREADS) void norm_finalize_kernel(const MatDesc* __restrict__ descs,
+                                                                   const int32_t* __restrict__ mats) {
   __shared__ double red[kWaves];
-  const MatDesc& d = descs[blockIdx.x];
+  const MatDesc& d = descs[mats[blockIdx.x]];
   double v = 0.0;
   for (int k = threadIdx.x; k < d.part_cnt; k += EW_THREADS) v += d.part[k];
   v = block_sum(v, red);
   if (threadIdx.x == 0) *d.scale = (float)(1.0 / (sqrt(v) + 1e-7));
 }
 
-hipError_t launch_momentum(const MatDesc* d, const EwItem* items, int n_items, int n_mats, float beta,
-                           hipStream_t s) {
+hipError_t launch_momentum(const MatDesc* d, const EwItem* items, int n_items, const int32_t* mats, int n_mats,
+                           float beta, hipStream_t s) {
   if (n_items == 0) return hipSuccess;
   momentum_kernel<<<n_items, EW_THREADS, 0, s>>>(d, items, beta);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  norm_finalize_kernel<<<n_mats, EW_THREADS, 0, s>>>(d);
+  norm_finalize_kernel<<<n_mats, EW_THREADS, 0, s>>>(d, mats);
   return hipGetLastError();
 }
 

@@ -99,11 +99,47 @@ struct AdamPlan {
   }
 };
 
+// Internal streams of a device's lanes, and the events that fork them from
+// and join them to the caller's stream.  Created on the first call with more
+// than one lane; default priority, non-blocking (ordered only by the events).
+struct LaneStreams {
+  bool ready = false;
+  hipStream_t s[kMaxLanes] = {};
+  hipEvent_t fork = nullptr;
+  hipEvent_t join[kMaxLanes] = {};
+
+  int create() {
+    if (ready) return MUON_OK;
+    hipError_t e;
+    for (int l = 0; l < kMaxLanes; ++l) {
+      if ((e = hipStreamCreateWithFlags(&s[l], hipStreamNonBlocking)) != hipSuccess) return fail_hip(e, "hipStreamCreateWithFlags");
+      if ((e = hipEventCreateWithFlags(&join[l], hipEventDisableTiming)) != hipSuccess) return fail_hip(e, "hipEventCreateWithFlags");
+    }
+    if ((e = hipEventCreateWithFlags(&fork, hipEventDisableTiming)) != hipSuccess) return fail_hip(e, "hipEventCreateWithFlags");
+    ready = true;
+    return MUON_OK;
+  }
+  void destroy() {
+    for (int l = 0; l < kMaxLanes; ++l) {
+      if (s[l]) (void)hipStreamDestroy(s[l]);
+      if (join[l]) (void)hipEventDestroy(join[l]);
+      s[l] = nullptr;
+      join[l] = nullptr;
+    }
+    if (fork) (void)hipEventDestroy(fork);
+    fork = nullptr;
+    ready = false;
+  }
+};
+
 struct DeviceState {
   HipOps ops;
   PlanCache cache{&ops};
   std::list<std::unique_ptr<AdamPlan>> adam_plans;  // most recent first
+  LaneStreams lanes;
 };
+
+int g_max_lanes = kDefaultLanes;
 
 std::map<int, std::unique_ptr<DeviceState>> g_dev;
 constexpr size_t kMaxAdamPlans = 8;
@@ -152,29 +188,32 @@ int capture_status(hipStream_t stream, bool* capturing) {
   return MUON_OK;
 }
 
-Tables tables_at(char* block, const PlanTables& t, char* ws) {
+Tables tables_at(char* block, const PlanTables& t, int lane, char* ws) {
+  const LaneTables& lt = t.lanes[lane];
   Tables v;
   v.desc = reinterpret_cast<MatDesc*>(block + t.o_desc);
-  v.mom = reinterpret_cast<EwItem*>(block + t.o_mom);
-  v.cast = reinterpret_cast<EwItem*>(block + t.o_cast);
-  v.apply = reinterpret_cast<EwItem*>(block + t.o_apply);
-  v.gram = reinterpret_cast<GemmItem*>(block + t.o_gram);
-  v.poly = reinterpret_cast<GemmItem*>(block + t.o_poly);
-  v.upd = reinterpret_cast<GemmItem*>(block + t.o_upd);
-  v.red = reinterpret_cast<RedItem*>(block + t.o_red);
+  v.mats = reinterpret_cast<int32_t*>(block + lt.o_mats);
+  v.mom = reinterpret_cast<EwItem*>(block + lt.o_mom);
+  v.cast = reinterpret_cast<EwItem*>(block + lt.o_cast);
+  v.apply = reinterpret_cast<EwItem*>(block + lt.o_apply);
+  v.gram = reinterpret_cast<GemmItem*>(block + lt.o_gram);
+  v.poly = reinterpret_cast<GemmItem*>(block + lt.o_poly);
+  v.upd = reinterpret_cast<GemmItem*>(block + lt.o_upd);
+  v.red = reinterpret_cast<RedItem*>(block + lt.o_red);
   v.gram_part = reinterpret_cast<float*>(ws + t.gram_part_off);
-  v.t = &t;
+  v.t = &lt;
   return v;
 }
 
-// The kernel sequence of one call: momentum and norm, cast, ns_steps
+// The kernel sequence of one lane: momentum and norm, cast, ns_steps
 // iterations of Gram, poly and update, apply.
 int launch_sequence(int mode, const Tables& v, float lr, float beta, int ns_steps, const float* coeffs, int stride,
                     hipStream_t stream) {
-  const PlanTables& t = *v.t;
+  const LaneTables& t = *v.t;
   int rc;
   if (mode == MODE_STEP) {
-    rc = timed(MUON_KERNEL_MOMENTUM, stream, [&] { return launch_momentum(v.desc, v.mom, t.n_mom, t.n_mat, beta, stream); },
+    rc = timed(MUON_KERNEL_MOMENTUM, stream,
+               [&] { return launch_momentum(v.desc, v.mom, t.n_mom, v.mats, t.n_mats, beta, stream); },
                "momentum kernel launch");
     if (rc) return rc;
   }
@@ -235,9 +274,31 @@ int run(int mode, float* const* params, const float* const* grads, float* const*
   DeviceState& st = device_state(dev);
   st.ops.stream = stream;
   Plan* p = nullptr;
-  if ((rc = st.cache.prepare(mode, shapes, n, recs, capturing, &p))) return rc;
-  return launch_sequence(mode, tables_at(static_cast<char*>(p->dev), p->t, p->ws), lr, beta, ns_steps, coeffs, stride,
-                         stream);
+  if ((rc = st.cache.prepare(mode, shapes, n, g_max_lanes, recs, capturing, &p))) return rc;
+  char* block = static_cast<char*>(p->dev);
+  const int L = (int)p->t.lanes.size();
+  if (L == 1 || capturing) {
+    // one lane, or under capture: every lane in turn on the caller's stream
+    for (int l = 0; l < L; ++l)
+      if ((rc = launch_sequence(mode, tables_at(block, p->t, l, p->ws), lr, beta, ns_steps, coeffs, stride, stream)))
+        return rc;
+    return MUON_OK;
+  }
+  // Several lanes: each runs its matrices' whole step on its own stream,
+  // after everything the caller enqueued before (the pointer patches
+  // included), and the caller's stream continues once all have finished.
+  LaneStreams& ls = st.lanes;
+  if ((rc = ls.create())) return rc;
+  if ((e = hipEventRecord(ls.fork, stream)) != hipSuccess) return fail_hip(e, "hipEventRecord(fork)");
+  for (int l = 0; l < L; ++l) {
+    if ((e = hipStreamWaitEvent(ls.s[l], ls.fork, 0)) != hipSuccess) return fail_hip(e, "hipStreamWaitEvent(fork)");
+    if ((rc = launch_sequence(mode, tables_at(block, p->t, l, p->ws), lr, beta, ns_steps, coeffs, stride, ls.s[l])))
+      return rc;
+    if ((e = hipEventRecord(ls.join[l], ls.s[l])) != hipSuccess) return fail_hip(e, "hipEventRecord(join)");
+  }
+  for (int l = 0; l < L; ++l)
+    if ((e = hipStreamWaitEvent(stream, ls.join[l], 0)) != hipSuccess) return fail_hip(e, "hipStreamWaitEvent(join)");
+  return MUON_OK;
 }
 
 int step_entry(float* const* params, const float* const* grads, float* const* momentum, const muon_shape_t* shapes,
@@ -504,6 +565,7 @@ void muon_release(void) {
     (void)hipDeviceSynchronize();
     kv.second->cache.release_all();
     kv.second->adam_plans.clear();
+    kv.second->lanes.destroy();
   }
   (void)hipSetDevice(cur);
   g_dev.clear();
@@ -522,6 +584,14 @@ int muon_plan_stats(int64_t out[6]) {
   const CacheStats& s = device_state(dev).cache.stats;
   const int64_t v[6] = {s.plan_builds, s.uploads, s.patch_calls, s.syncs, s.evictions, s.ws_allocs};
   for (int k = 0; k < 6; ++k) out[k] = v[k];
+  return MUON_OK;
+}
+
+int muon_set_lanes(int lanes) {
+  clear_error();
+  if (lanes < 1 || lanes > kMaxLanes) return fail(MUON_EINVAL, "lanes = %d outside [1, %d]", lanes, kMaxLanes);
+  std::lock_guard<std::mutex> lock(api_mutex());
+  g_max_lanes = lanes;
   return MUON_OK;
 }
 

@@ -93,7 +93,7 @@ int noalloc_entry(float* const* params, const float* const* grads, float* const*
   // them (under capture always, so that a replay finds its own).
   if (!(sc.known && sc.table_key == key)) {
     PlanTables t;
-    if ((rc = build_tables(MODE_STEP, shapes, n, base, &t))) return rc;
+    if ((rc = build_tables(MODE_STEP, shapes, n, base, 1, &t))) return rc;
     const size_t off = align_up(ws_need);
     if (off + t.image.size() > (size_t)MUON_NOALLOC_SCRATCH_BYTES)
       return fail(MUON_ENOMEM, "this call needs %zu bytes of workspace and tables; the static scratch holds %zu",
@@ -115,7 +115,7 @@ int noalloc_entry(float* const* params, const float* const* grads, float* const*
   }
   // after a capture the device holds whatever the last replay wrote
   sc.known = !capturing;
-  return launch_sequence(MODE_STEP, tables_at(base + sc.table_off, sc.tables, base), lr, beta, ns_steps, coeffs, 0,
+  return launch_sequence(MODE_STEP, tables_at(base + sc.table_off, sc.tables, 0, base), lr, beta, ns_steps, coeffs, 0,
                          stream);
 }
 

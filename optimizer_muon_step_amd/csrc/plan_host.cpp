@@ -280,16 +280,56 @@ size_t workspace_bytes_of(const muon_shape_t* shapes, int n) {
   return total;
 }
 
-int build_tables(int mode, const muon_shape_t* shapes, int n, char* ws_base, PlanTables* out) {
+std::vector<int> lane_of_matrices(const muon_shape_t* shapes, int n, int max_lanes) {
+  std::vector<int> lane(n, 0);
+  if (max_lanes <= 1 || n <= 1) return lane;
+  // shape groups and their Newton-Schulz cost (m^2 n terms)
+  std::vector<std::pair<int64_t, int64_t>> key(n);
+  std::vector<std::pair<std::pair<int64_t, int64_t>, double>> groups;
+  for (int i = 0; i < n; ++i) {
+    const Geometry g = geometry_of(shapes[i]);
+    key[i] = {g.m, g.n};
+    const double cost = (double)g.m * g.m * (3.0 * g.n + g.m);
+    size_t k = 0;
+    while (k < groups.size() && groups[k].first != key[i]) ++k;
+    if (k == groups.size()) groups.push_back({key[i], 0.0});
+    groups[k].second += cost;
+  }
+  const int lanes = std::min<int>(std::min(max_lanes, kMaxLanes), (int)groups.size());
+  std::stable_sort(groups.begin(), groups.end(), [](const auto& a, const auto& b) { return a.second > b.second; });
+  std::vector<double> load(lanes, 0.0);
+  std::vector<int> group_lane(groups.size());
+  for (size_t k = 0; k < groups.size(); ++k) {
+    const int l = (int)(std::min_element(load.begin(), load.end()) - load.begin());
+    group_lane[k] = l;
+    load[l] += groups[k].second;
+  }
+  for (int i = 0; i < n; ++i)
+    for (size_t k = 0; k < groups.size(); ++k)
+      if (groups[k].first == key[i]) lane[i] = group_lane[k];
+  return lane;
+}
+
+int build_tables(int mode, const muon_shape_t* shapes, int n, char* ws_base, int max_lanes, PlanTables* out) {
   PlanTables& T = *out;
+  const std::vector<int> lane_of = lane_of_matrices(shapes, n, max_lanes);
+  const int L = n ? *std::max_element(lane_of.begin(), lane_of.end()) + 1 : 1;
+  struct Lists {
+    std::vector<int32_t> mats;
+    std::vector<EwItem> mom, cast, apply;
+    std::vector<GemmItem> gram_seq, poly_seq, upd_seq;
+    std::vector<int64_t> gram_cost, upd_cost;
+    std::vector<RedItem> red;
+  };
+  std::vector<Lists> lists(L);
   std::vector<MatDesc> desc(n);
-  std::vector<EwItem> mom, cast, apply;
   char* cur = ws_base;
   float* scales = reinterpret_cast<float*>(cur);
   cur += kControlBytes;
   for (int i = 0; i < n; ++i) {
     const Geometry g = geometry_of(shapes[i]);
     MatDesc& d = desc[i];
+    Lists& li = lists[lane_of[i]];
     memset(&d, 0, sizeof d);
     d.X[0] = carve<uint16_t>(cur, g.x_bytes / 2);
     d.X[1] = carve<uint16_t>(cur, g.x_bytes / 2);
@@ -307,18 +347,20 @@ int build_tables(int mode, const muon_shape_t* shapes, int n, char* ws_base, Pla
     d.ld_a = g.ld_a;
     d.transposed = g.transposed;
     d.part_cnt = g.part_cnt;
+    li.mats.push_back(i);
     if (mode == MODE_STEP)
-      for (int c = 0; c < g.part_cnt; ++c) mom.push_back({i, c});
+      for (int c = 0; c < g.part_cnt; ++c) li.mom.push_back({i, c});
     const int ct = (g.m_pad / CAST_TILE) * (g.n_pad / CAST_TILE);
-    for (int t = 0; t < ct; ++t) cast.push_back({i, t});
+    for (int t = 0; t < ct; ++t) li.cast.push_back({i, t});
     const int at = ((g.rows + CAST_TILE - 1) / CAST_TILE) * ((g.cols + CAST_TILE - 1) / CAST_TILE);
-    for (int t = 0; t < at; ++t) apply.push_back({i, t});
+    for (int t = 0; t < at; ++t) li.apply.push_back({i, t});
   }
   // The cast re-reads what the momentum pass just streamed: walking it
   // backwards starts with the lines most likely still in the memory-side
   // cache.
-  std::reverse(cast.begin(), cast.end());
-  // Partial tiles of split Gram tiles follow the matrices' buffers.
+  for (Lists& li : lists) std::reverse(li.cast.begin(), li.cast.end());
+  // Partial tiles of split Gram tiles follow the matrices' buffers; the
+  // split is decided over the whole call.
   const GramSplit split = gram_split_of(shapes, n);
   T.gram_part_off = (size_t)(cur - ws_base);
   (void)carve<float>(cur, (size_t)split.slots * GRAM_BM * GRAM_BM);
@@ -327,51 +369,43 @@ int build_tables(int mode, const muon_shape_t* shapes, int n, char* ws_base, Pla
   // phases: upper-triangle tiles row by row), then spread over the XCDs.
   // Gram and poly tiles differ in size (256 and 128); a long-K Gram tile may
   // be cut into K chunks, each its own item, summed by the reduce pass.
-  std::vector<GemmItem> gram_seq, poly_seq, upd_seq;
-  std::vector<RedItem> red;
-  std::vector<int64_t> gram_cost, upd_cost;
   int32_t slot = 0;
   for (int i = 0; i < n; ++i) {
+    Lists& li = lists[lane_of[i]];
     const int tg = desc[i].m_pad / GRAM_BM, tm = desc[i].m_pad / SYM_BM, tn = desc[i].n_pad / UPD_BN;
     const int64_t ks = ((int64_t)desc[i].n + 63) / 64;                   // Gram K slices
-    const int32_t kp = (int32_t)(((int64_t)desc[i].m + 63) / 64);          // poly K slices
+    const int32_t kp = (int32_t)(((int64_t)desc[i].m + SYM_BK - 1) / SYM_BK);  // poly K slices
     const int32_t ku = (int32_t)(2 * (((int64_t)desc[i].m + 127) / 128));  // update: even, see the kernel
     const int64_t nc = gram_chunks(ks, split.chunk);
     for (int ti = 0; ti < tg; ++ti)
       for (int tj = ti; tj < tg; ++tj) {
         if (nc == 1) {
-          gram_seq.push_back({i, (int16_t)ti, (int16_t)tj, 0, (int32_t)ks, -1});
-          gram_cost.push_back(ks);
+          li.gram_seq.push_back({i, (int16_t)ti, (int16_t)tj, 0, (int32_t)ks, -1});
+          li.gram_cost.push_back(ks);
           continue;
         }
         for (int64_t c = 0; c < nc; ++c) {
           const int64_t a = ks * c / nc, b = ks * (c + 1) / nc;
-          gram_seq.push_back({i, (int16_t)ti, (int16_t)tj, (int32_t)a, (int32_t)(b - a), slot + (int32_t)c});
-          gram_cost.push_back(b - a);
+          li.gram_seq.push_back({i, (int16_t)ti, (int16_t)tj, (int32_t)a, (int32_t)(b - a), slot + (int32_t)c});
+          li.gram_cost.push_back(b - a);
         }
         constexpr int SUB = GRAM_BM / RED_TILE;
         for (int bi = 0; bi < SUB; ++bi)
           for (int bj = 0; bj < SUB; ++bj)
-            if (ti != tj || bi <= bj) red.push_back({i, (int16_t)ti, (int16_t)tj, slot, (int16_t)nc, (int8_t)bi, (int8_t)bj});
+            if (ti != tj || bi <= bj)
+              li.red.push_back({i, (int16_t)ti, (int16_t)tj, slot, (int16_t)nc, (int8_t)bi, (int8_t)bj});
         slot += (int32_t)nc;
       }
     for (int ti = 0; ti < tm; ++ti)
-      for (int tj = ti; tj < tm; ++tj) poly_seq.push_back({i, (int16_t)ti, (int16_t)tj, 0, kp, -1});
+      for (int tj = ti; tj < tm; ++tj) li.poly_seq.push_back({i, (int16_t)ti, (int16_t)tj, 0, kp, -1});
     for (int tj = 0; tj < tn; ++tj)
       for (int ti = 0; ti < desc[i].m_pad / UPD_ROWU; ti += UPD_BM / UPD_ROWU) {
-        upd_seq.push_back({i, (int16_t)ti, (int16_t)tj, 0, ku, -1});
-        upd_cost.push_back(ku);
+        li.upd_seq.push_back({i, (int16_t)ti, (int16_t)tj, 0, ku, -1});
+        li.upd_cost.push_back(ku);
       }
   }
   if (slot != split.slots)
     return fail(MUON_EINVAL, "internal: %d Gram partial tiles planned, %lld sized", slot, (long long)split.slots);
-  std::vector<int64_t> poly_cost(poly_seq.size());
-  for (size_t k = 0; k < poly_seq.size(); ++k) poly_cost[k] = poly_seq[k].kn;
-  const std::vector<GemmItem> gram = xcd_interleave(gram_seq, gram_cost);
-  const std::vector<GemmItem> poly = xcd_interleave(poly_seq, poly_cost);
-  const std::vector<GemmItem> updl = xcd_interleave(upd_seq, upd_cost);
-  const size_t lists = mom.size() + cast.size() + apply.size() + gram.size() + poly.size() + updl.size() + red.size();
-  if (lists > (size_t)INT32_MAX / 2) return fail(MUON_EINVAL, "call of %zu work items is too large", lists);
 
   size_t off = 0;
   auto place = [&](size_t bytes) {
@@ -380,34 +414,56 @@ int build_tables(int mode, const muon_shape_t* shapes, int n, char* ws_base, Pla
     return o;
   };
   T.o_desc = place(sizeof(MatDesc) * n);
-  T.o_mom = place(sizeof(EwItem) * mom.size());
-  T.o_cast = place(sizeof(EwItem) * cast.size());
-  T.o_apply = place(sizeof(EwItem) * apply.size());
-  T.o_gram = place(sizeof(GemmItem) * gram.size());
-  T.o_poly = place(sizeof(GemmItem) * poly.size());
-  T.o_upd = place(sizeof(GemmItem) * updl.size());
-  T.o_red = place(sizeof(RedItem) * red.size());
+  T.n_mat = n;
+  T.lanes.assign(L, LaneTables{});
+  std::vector<std::vector<GemmItem>> gram(L), poly(L), upd(L);
+  size_t items = 0;
+  for (int l = 0; l < L; ++l) {
+    Lists& li = lists[l];
+    std::vector<int64_t> poly_cost(li.poly_seq.size());
+    for (size_t k = 0; k < li.poly_seq.size(); ++k) poly_cost[k] = li.poly_seq[k].kn;
+    gram[l] = xcd_interleave(li.gram_seq, li.gram_cost);
+    poly[l] = xcd_interleave(li.poly_seq, poly_cost);
+    upd[l] = xcd_interleave(li.upd_seq, li.upd_cost);
+    LaneTables& lt = T.lanes[l];
+    lt.o_mats = place(sizeof(int32_t) * li.mats.size());
+    lt.o_mom = place(sizeof(EwItem) * li.mom.size());
+    lt.o_cast = place(sizeof(EwItem) * li.cast.size());
+    lt.o_apply = place(sizeof(EwItem) * li.apply.size());
+    lt.o_gram = place(sizeof(GemmItem) * gram[l].size());
+    lt.o_poly = place(sizeof(GemmItem) * poly[l].size());
+    lt.o_upd = place(sizeof(GemmItem) * upd[l].size());
+    lt.o_red = place(sizeof(RedItem) * li.red.size());
+    lt.n_mats = (int)li.mats.size();
+    lt.n_mom = (int)li.mom.size();
+    lt.n_cast = (int)li.cast.size();
+    lt.n_apply = (int)li.apply.size();
+    lt.n_gram = (int)gram[l].size();
+    lt.n_poly = (int)poly[l].size();
+    lt.n_upd = (int)upd[l].size();
+    lt.n_red = (int)li.red.size();
+    items += li.mom.size() + li.cast.size() + li.apply.size() + gram[l].size() + poly[l].size() + upd[l].size() +
+             li.red.size();
+  }
+  if (items > (size_t)INT32_MAX / 2) return fail(MUON_EINVAL, "call of %zu work items is too large", items);
   T.image.assign(std::max<size_t>(off, kAlign), 0);
   char* h = T.image.data();
   auto put = [&](size_t o, const void* src, size_t bytes) {
     if (bytes) memcpy(h + o, src, bytes);
   };
   put(T.o_desc, desc.data(), sizeof(MatDesc) * n);
-  put(T.o_mom, mom.data(), sizeof(EwItem) * mom.size());
-  put(T.o_cast, cast.data(), sizeof(EwItem) * cast.size());
-  put(T.o_apply, apply.data(), sizeof(EwItem) * apply.size());
-  put(T.o_gram, gram.data(), sizeof(GemmItem) * gram.size());
-  put(T.o_poly, poly.data(), sizeof(GemmItem) * poly.size());
-  put(T.o_upd, updl.data(), sizeof(GemmItem) * updl.size());
-  put(T.o_red, red.data(), sizeof(RedItem) * red.size());
-  T.n_mat = n;
-  T.n_mom = (int)mom.size();
-  T.n_cast = (int)cast.size();
-  T.n_apply = (int)apply.size();
-  T.n_gram = (int)gram.size();
-  T.n_poly = (int)poly.size();
-  T.n_upd = (int)updl.size();
-  T.n_red = (int)red.size();
+  for (int l = 0; l < L; ++l) {
+    const Lists& li = lists[l];
+    const LaneTables& lt = T.lanes[l];
+    put(lt.o_mats, li.mats.data(), sizeof(int32_t) * li.mats.size());
+    put(lt.o_mom, li.mom.data(), sizeof(EwItem) * li.mom.size());
+    put(lt.o_cast, li.cast.data(), sizeof(EwItem) * li.cast.size());
+    put(lt.o_apply, li.apply.data(), sizeof(EwItem) * li.apply.size());
+    put(lt.o_gram, gram[l].data(), sizeof(GemmItem) * gram[l].size());
+    put(lt.o_poly, poly[l].data(), sizeof(GemmItem) * poly[l].size());
+    put(lt.o_upd, upd[l].data(), sizeof(GemmItem) * upd[l].size());
+    put(lt.o_red, li.red.data(), sizeof(RedItem) * li.red.size());
+  }
   return MUON_OK;
 }
 
@@ -526,13 +582,14 @@ int PlanCache::set_workspace(void* p, size_t bytes) {
   return MUON_OK;
 }
 
-int PlanCache::prepare(int mode, const muon_shape_t* shapes, int n, const std::vector<PtrRecord>& recs,
+int PlanCache::prepare(int mode, const muon_shape_t* shapes, int n, int max_lanes, const std::vector<PtrRecord>& recs,
                        bool capturing, Plan** out) {
   int rc = acquire_workspace(workspace_bytes_of(shapes, n), capturing);
   if (rc) return rc;
   std::vector<int64_t> key;
-  key.reserve(3 + 2 * (size_t)n);
+  key.reserve(4 + 2 * (size_t)n);
   key.push_back(mode);
+  key.push_back(max_lanes);
   key.push_back(n);
   key.push_back((int64_t)(uintptr_t)ws_);
   for (int i = 0; i < n; ++i) {
@@ -553,7 +610,7 @@ int PlanCache::prepare(int mode, const muon_shape_t* shapes, int n, const std::v
     auto p = std::make_unique<Plan>();
     p->key = std::move(key);
     p->ws = ws_;
-    if ((rc = build_tables(mode, shapes, n, ws_, &p->t))) return rc;
+    if ((rc = build_tables(mode, shapes, n, ws_, max_lanes, &p->t))) return rc;
     if ((rc = ops_->alloc_tables(p->t.image.size(), &p->dev, &p->host))) return rc;
     if ((rc = ops_->upload(p->dev, p->host, p->t.image.data(), p->t.image.size()))) {
       free_plan(p.get());

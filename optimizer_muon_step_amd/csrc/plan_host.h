@@ -54,15 +54,33 @@ size_t workspace_bytes_of(const muon_shape_t* shapes, int n);
 
 enum Mode { MODE_STEP = 0, MODE_NS = 1 };
 
+// Work lists of one lane: a group of matrices whose whole step runs as one
+// launch sequence (on a stream of its own when a call has several lanes).
+struct LaneTables {
+  size_t o_mats = 0, o_mom = 0, o_cast = 0, o_apply = 0, o_gram = 0, o_poly = 0, o_upd = 0, o_red = 0;
+  int n_mats = 0, n_mom = 0, n_cast = 0, n_apply = 0, n_gram = 0, n_poly = 0, n_upd = 0, n_red = 0;
+};
+
 // Host image of a plan's device table block: descriptors (workspace pointers
-// filled in, caller pointers left null) followed by the work lists.
+// filled in, caller pointers left null) followed by each lane's matrix list
+// and work lists.
 struct PlanTables {
   std::vector<char> image;
-  size_t o_desc = 0, o_mom = 0, o_cast = 0, o_apply = 0, o_gram = 0, o_poly = 0, o_upd = 0, o_red = 0;
-  int n_mat = 0, n_mom = 0, n_cast = 0, n_apply = 0, n_gram = 0, n_poly = 0, n_upd = 0, n_red = 0;
+  size_t o_desc = 0;
+  int n_mat = 0;
+  std::vector<LaneTables> lanes;
   size_t gram_part_off = 0;  // Gram partial tiles, offset in the workspace
 };
-int build_tables(int mode, const muon_shape_t* shapes, int n, char* ws_base, PlanTables* out);
+
+// Lanes: matrices of one canonical shape always share a lane; shape groups
+// are spread over at most max_lanes lanes, largest Newton-Schulz cost first
+// onto the least loaded lane.  The long-K Gram split is decided over the
+// whole call, so the lanes change only which launch a tile belongs to, never
+// a result.
+constexpr int kMaxLanes = 4;
+constexpr int kDefaultLanes = 1;
+std::vector<int> lane_of_matrices(const muon_shape_t* shapes, int n, int max_lanes);
+int build_tables(int mode, const muon_shape_t* shapes, int n, char* ws_base, int max_lanes, PlanTables* out);
 
 // The caller pointers of one call, one record per matrix (mat = index).
 void make_ptr_records(int mode, const muon_shape_t* shapes, int n, float* const* params, const float* const* grads,
@@ -123,8 +141,8 @@ class PlanCache {
   PlanCache(const PlanCache&) = delete;
   PlanCache& operator=(const PlanCache&) = delete;
 
-  int prepare(int mode, const muon_shape_t* shapes, int n, const std::vector<PtrRecord>& recs, bool capturing,
-              Plan** out);
+  int prepare(int mode, const muon_shape_t* shapes, int n, int max_lanes, const std::vector<PtrRecord>& recs,
+              bool capturing, Plan** out);
   // Caller-owned workspace (nullptr / 0: back to library-owned).
   int set_workspace(void* p, size_t bytes);
   // Frees every plan and workspace (the caller has synchronised).

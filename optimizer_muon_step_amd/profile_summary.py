@@ -1,6 +1,6 @@
 """Summaries of rocprofv3 output for the committed profiles.
 
-Two subcommands, each reading the CSV files rocprofv3 writes with
+Three subcommands, each reading the CSV files rocprofv3 writes with
 `--output-format csv -o run`:
 
   trace   <dir> <out.md> --command CMD
@@ -13,6 +13,12 @@ Two subcommands, each reading the CSV files rocprofv3 writes with
       bench.py after its timed region): factor = known bytes / counted bytes.
       The JSON holds the figure bench.py reports as `roofline.traffic` for the
       update GEMM, tagged with the sha256 of the kernel source it was taken on.
+
+  mfma    <pmc_dir> <trace_dir> <out.md> --command CMD
+      Matrix-core use of the Newton-Schulz GEMMs on the GPT-2-124M hidden set
+      from one pass with SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_BF16,
+      SQ_BUSY_CYCLES and GRBM_GUI_ACTIVE, with the kernel durations of a
+      separate trace run beside it.
 
 FETCH_SIZE and WRITE_SIZE count traffic between the L2 caches and the memory
 fabric, so reads served by the memory-side cache count as fetched.
@@ -80,7 +86,8 @@ def cmd_trace(args):
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                      f"{100 * float(r['TotalDurationNs']) / total:.1f}% |")
     for w in args.window or []:
-        fam, first, count = w.split(":")
+        fam, first, count, *label = w.split(":", 3)
+        label = label[0] if label else "the benchmark's timed region"
         first, count = int(first), int(count)
         trace = [r for r in csv.DictReader(open(os.path.join(args.dir, "run_kernel_trace.csv")))
                  if family(r["Kernel_Name"]) == fam]
@@ -91,8 +98,8 @@ def cmd_trace(args):
         durs = sorted((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in sel)
         mean = sum(durs) / count
         median = (durs[(count - 1) // 2] + durs[count // 2]) / 2
-        lines += ["", f"{fam} launches {first + 1}-{first + count} (in dispatch order; the benchmark's timed "
-                      f"region): mean {mean:.2f} us, median {median:.2f} us over {count} launches."]
+        lines += ["", f"{fam} launches {first + 1}-{first + count} (in dispatch order; {label}): "
+                      f"mean {mean:.2f} us, median {median:.2f} us over {count} launches."]
     open(args.out, "w").write("\n".join(lines) + "\n")
 
 
@@ -152,6 +159,91 @@ def cmd_traffic(args):
     open(args.out_md, "w").write("\n".join(lines) + "\n")
 
 
+def read_dispatch_counters(d: str):
+    """{dispatch_id: (kernel name, {counter: value})}; the CSV holds one value
+    per dispatch and counter, summed over the counter's hardware instances."""
+    out = {}
+    with open(os.path.join(d, "run_counter_collection.csv")) as f:
+        for r in csv.DictReader(f):
+            key = int(r["Dispatch_Id"])
+            name, vals = out.setdefault(key, (r["Kernel_Name"], collections.defaultdict(float)))
+            vals[r["Counter_Name"]] += float(r["Counter_Value"])
+    return out
+
+
+def gpu_agent(d: str):
+    with open(os.path.join(d, "run_agent_info.csv")) as f:
+        for r in csv.DictReader(f):
+            if r["Agent_Type"] == "GPU":
+                return {"xcc": int(r["Num_Xcc"]), "simd": int(r["Simd_Count"]), "cu": int(r["Cu_Count"]),
+                        "max_clk_mhz": float(r["Max_Engine_Clk_Fcompute"]), "target": r.get("Name", "")}
+    raise SystemExit("no GPU agent in run_agent_info.csv")
+
+
+def c3_ns_flops():
+    """Algorithmic flops per launch of each Newton-Schulz GEMM on the
+    GPT-2-124M hidden set (symmetry of X X^T and of A A counted once)."""
+    from optimizer_muon_step_amd import workloads as wl
+    gram = poly = upd = 0
+    for s in wl.config_specs("c3"):
+        m, n = min(s.rows, s.cols), max(s.rows, s.cols)
+        gram += m * (m + 1) * n
+        poly += m * m * (m + 1)
+        upd += 2 * m * m * n
+    return {"ns_gram": gram, "ns_poly": poly, "ns_update": upd}
+
+
+def cmd_mfma(args):
+    agent = gpu_agent(args.pmc_dir)
+    disp = read_dispatch_counters(args.pmc_dir)
+    trace = collections.defaultdict(list)
+    for r in csv.DictReader(open(os.path.join(args.trace_dir, "run_kernel_trace.csv"))):
+        trace[family(r["Kernel_Name"])].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
+    algo = c3_ns_flops()
+    peak = 2.5e15
+    lines = [f"# {args.title}", "", "Commands (from the repository root on an MI355X):", "", "```", args.command, "```", "",
+             f"GPU: {agent['cu']} CUs, {agent['simd']} SIMDs, {agent['xcc']} XCDs, maximum engine clock "
+             f"{agent['max_clk_mhz']:.0f} MHz.", "",
+             "Normalisation.  SQ_VALU_MFMA_BUSY_CYCLES is summed over all SIMDs; GRBM_GUI_ACTIVE counts the "
+             f"cycles the GPU was active in each of the {agent['xcc']} XCDs and the CSV holds their sum, so the "
+             "kernel's active cycles are that sum / XCDs (rocprofv3's own MfmaUtil metric takes the per-XCD "
+             "maximum).  MFMA utilisation = busy cycles / (active cycles x SIMDs): the fraction of the matrix "
+             "pipes' cycles spent on MFMA work at the clock the kernel ran at.  Executed flops = "
+             "SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512.  The effective clock is active cycles / the kernel's mean "
+             "duration in the trace run; utilisation x effective clock / 2.4 GHz x (algorithmic / executed "
+             "flops) is the fraction of the 2.5 PFLOP/s bf16 peak the algorithmic flops reach, to be compared "
+             "with algorithmic flops / trace duration / 2.5 PFLOP/s.", "",
+             "| Kernel | Dispatches | Active cycles / dispatch | MFMA busy (SIMD-cycles) | MFMA utilisation | "
+             "Executed GFLOP | Algorithmic GFLOP | Trace mean (us) | Effective clock (GHz) | "
+             "Peak fraction from counters | Peak fraction from trace |",
+             "|:--|--:|--:|--:|--:|--:|--:|--:|--:|--:|--:|"]
+    for fam in ("ns_update", "ns_gram", "ns_poly"):
+        rows = [v for n, v in disp.values() if family(n) == fam]
+        if not rows:
+            raise SystemExit(f"no {fam} dispatch in the counter run")
+        k = len(rows)
+        busy = sum(v["SQ_VALU_MFMA_BUSY_CYCLES"] for v in rows) / k
+        mops = sum(v["SQ_INSTS_VALU_MFMA_MOPS_BF16"] for v in rows) / k
+        active = sum(v["GRBM_GUI_ACTIVE"] for v in rows) / k / agent["xcc"]
+        util = busy / (active * agent["simd"])
+        executed = 512.0 * mops
+        durs = trace.get(fam)
+        if not durs:
+            raise SystemExit(f"no {fam} launch in the trace run")
+        dur = sum(durs) / len(durs)
+        clock = active / dur
+        frac_counters = util * clock / 2.4e9 * algo[fam] / executed
+        frac_trace = algo[fam] / dur / peak
+        lines.append(f"| {fam} | {k} | {active:,.0f} | {busy:,.0f} | {100 * util:.1f}% | {executed / 1e9:.2f} | "
+                     f"{algo[fam] / 1e9:.2f} | {dur * 1e6:.2f} | {clock / 1e9:.2f} | {frac_counters:.3f} | "
+                     f"{frac_trace:.3f} |")
+    lines += ["", f"Update-kernel fingerprint (sha256 of ns_gemm_tile.h, kernels_ns.hip and their build options): "
+                  f"`{update_kernel_fingerprint()}`"]
+    if args.note:
+        lines += ["", args.note]
+    open(args.out, "w").write("\n".join(lines) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -162,7 +254,7 @@ def main():
     t.add_argument("--title", default="Kernel trace summary")
     t.add_argument("--note", default="")
     t.add_argument("--window", action="append",
-                   help="FAMILY:FIRST:COUNT, mean duration of that family's launches FIRST..FIRST+COUNT-1")
+                   help="FAMILY:FIRST:COUNT[:LABEL], mean duration of that family's launches FIRST..FIRST+COUNT-1")
     r = sub.add_parser("traffic")
     r.add_argument("fetch_dir")
     r.add_argument("write_dir")
@@ -170,8 +262,15 @@ def main():
     r.add_argument("out_md")
     r.add_argument("--command", required=True)
     r.add_argument("--title", default="HBM traffic per dispatch")
+    m = sub.add_parser("mfma")
+    m.add_argument("pmc_dir")
+    m.add_argument("trace_dir")
+    m.add_argument("out")
+    m.add_argument("--command", required=True)
+    m.add_argument("--title", default="Matrix-core use of the Newton-Schulz GEMMs")
+    m.add_argument("--note", default="")
     args = ap.parse_args()
-    (cmd_trace if args.cmd == "trace" else cmd_traffic)(args)
+    {"trace": cmd_trace, "traffic": cmd_traffic, "mfma": cmd_mfma}[args.cmd](args)
 
 
 if __name__ == "__main__":

@@ -156,14 +156,39 @@ static void check_tables(const Plan& p, const std::vector<muon_shape_t>& s, size
   }
   std::sort(regions.begin(), regions.end());
   for (size_t k = 1; k < regions.size(); ++k) CHECK(regions[k].first >= regions[k - 1].second);
-  CHECK(t.n_mom == mom && t.n_cast == cast && t.n_apply == apply);
-  // elementwise items: each (matrix, index) once, indices in range
-  auto ew = [&](size_t off, int cnt, int which) {
+  // every matrix in exactly one lane's list; lanes hold whole shape groups
+  std::vector<int> lane_of(n, -1);
+  int64_t n_mom = 0, n_cast = 0, n_apply = 0;
+  for (size_t l = 0; l < t.lanes.size(); ++l) {
+    const LaneTables& lt = t.lanes[l];
+    const int32_t* mats = p.at<int32_t>(lt.o_mats);
+    CHECK(lt.n_mats >= 1);
+    for (int k = 0; k < lt.n_mats; ++k) {
+      CHECK(mats[k] >= 0 && mats[k] < n);
+      if (mats[k] < 0 || mats[k] >= n) continue;
+      CHECK(lane_of[mats[k]] == -1);
+      lane_of[mats[k]] = (int)l;
+    }
+    n_mom += lt.n_mom;
+    n_cast += lt.n_cast;
+    n_apply += lt.n_apply;
+  }
+  for (int i = 0; i < n; ++i) {
+    CHECK(lane_of[i] >= 0);
+    for (int j = 0; j < n; ++j) {
+      const Geometry a = geometry_of(s[i]), b = geometry_of(s[j]);
+      if (a.m == b.m && a.n == b.n) CHECK(lane_of[i] == lane_of[j]);
+    }
+  }
+  CHECK(n_mom == mom && n_cast == cast && n_apply == apply);
+  // elementwise items: each (matrix, index) once over all lanes, in the
+  // lane of its matrix, indices in range
+  auto ew = [&](size_t off, int cnt, int which, int lane, std::set<std::pair<int, int>>& seen) {
     const EwItem* it = p.at<EwItem>(off);
-    std::set<std::pair<int, int>> seen;
     for (int k = 0; k < cnt; ++k) {
       CHECK(it[k].mat >= 0 && it[k].mat < n);
       if (it[k].mat < 0 || it[k].mat >= n) continue;
+      CHECK(lane_of[it[k].mat] == lane);
       const Geometry g = geometry_of(s[it[k].mat]);
       const int lim = which == 0 ? g.part_cnt
                       : which == 1 ? (g.m_pad / CAST_TILE) * (g.n_pad / CAST_TILE)
@@ -172,54 +197,60 @@ static void check_tables(const Plan& p, const std::vector<muon_shape_t>& s, size
       CHECK(seen.insert({it[k].mat, it[k].idx}).second);
     }
   };
-  ew(t.o_mom, t.n_mom, 0);
-  ew(t.o_cast, t.n_cast, 1);
-  ew(t.o_apply, t.n_apply, 2);
+  std::set<std::pair<int, int>> seen_mom, seen_cast, seen_apply;
+  for (size_t l = 0; l < t.lanes.size(); ++l) {
+    ew(t.lanes[l].o_mom, t.lanes[l].n_mom, 0, (int)l, seen_mom);
+    ew(t.lanes[l].o_cast, t.lanes[l].n_cast, 1, (int)l, seen_cast);
+    ew(t.lanes[l].o_apply, t.lanes[l].n_apply, 2, (int)l, seen_apply);
+  }
   // GEMM items: tiles inside the padded matrix, K ranges inside the true
   // size, each output tile covered once per kind (Gram chunks tile K)
-  auto gemm = [&](size_t off, int cnt, int kind) {
+  std::map<std::tuple<int, int, int>, int64_t> ksum[3];
+  auto gemm = [&](size_t off, int cnt, int kind, int lane) {
     const GemmItem* it = p.at<GemmItem>(off);
     CHECK(cnt % 8 == 0);
-    std::map<std::tuple<int, int, int>, int64_t> ksum;
     for (int k = 0; k < cnt; ++k) {
       if (it[k].mat < 0) continue;
       CHECK(it[k].mat < n);
+      if (it[k].mat >= n) continue;
+      CHECK(lane_of[it[k].mat] == lane);
       const MatDesc& m = d[it[k].mat];
       if (kind == 0) {
         CHECK(it[k].ti <= it[k].tj && (it[k].tj + 1) * GRAM_BM <= m.m_pad);
         CHECK(it[k].k0 >= 0 && (int64_t)(it[k].k0 + it[k].kn) * 64 <= m.n_pad && it[k].kn >= 1);
-        ksum[{it[k].mat, it[k].ti, it[k].tj}] += it[k].kn;
+        ksum[0][{it[k].mat, it[k].ti, it[k].tj}] += it[k].kn;
+        if (it[k].slot >= 0) {
+          const char* lo = p.ws + t.gram_part_off + (size_t)it[k].slot * GRAM_BM * GRAM_BM * 4;
+          CHECK(lo >= p.ws && lo + GRAM_BM * GRAM_BM * 4 <= ws_hi);
+        }
       } else if (kind == 1) {
-        CHECK(it[k].ti <= it[k].tj && (it[k].tj + 1) * SYM_BM <= m.m_pad && it[k].kn * 64 <= m.m_pad);
-        ksum[{it[k].mat, it[k].ti, it[k].tj}] += 1;
+        CHECK(it[k].ti <= it[k].tj && (it[k].tj + 1) * SYM_BM <= m.m_pad && it[k].kn * SYM_BK <= m.m_pad);
+        CHECK((int64_t)it[k].kn * SYM_BK >= m.m);
+        ksum[1][{it[k].mat, it[k].ti, it[k].tj}] += 1;
       } else {
         CHECK(it[k].ti * UPD_ROWU < m.m_pad && (it[k].tj + 1) * UPD_BN <= m.n_pad);
         CHECK(it[k].kn % 2 == 0 && it[k].kn * 64 <= m.m_pad);
         CHECK(it[k].ti * UPD_ROWU + UPD_BM <= m.m_pad + NS_PAD_M);  // overhang inside the spare rows
-        ksum[{it[k].mat, it[k].ti, it[k].tj}] += 1;
+        ksum[2][{it[k].mat, it[k].ti, it[k].tj}] += 1;
       }
     }
-    for (auto& kv : ksum) {
-      const MatDesc& m = d[std::get<0>(kv.first)];
-      if (kind == 0) CHECK(kv.second == ((int64_t)m.n + 63) / 64);
-      else CHECK(kv.second == 1);
-    }
-    if (kind == 1) {
-      int64_t want = 0;
-      for (int i = 0; i < n; ++i) want += (int64_t)(d[i].m_pad / SYM_BM) * (d[i].m_pad / SYM_BM + 1) / 2;
-      CHECK((int64_t)ksum.size() == want);
-    }
   };
-  gemm(t.o_gram, t.n_gram, 0);
-  gemm(t.o_poly, t.n_poly, 1);
-  gemm(t.o_upd, t.n_upd, 2);
-  // partial tiles of cut Gram tiles lie inside the workspace
-  const GemmItem* g = p.at<GemmItem>(t.o_gram);
-  for (int k = 0; k < t.n_gram; ++k)
-    if (g[k].mat >= 0 && g[k].slot >= 0) {
-      const char* lo = p.ws + t.gram_part_off + (size_t)g[k].slot * GRAM_BM * GRAM_BM * 4;
-      CHECK(lo >= p.ws && lo + GRAM_BM * GRAM_BM * 4 <= ws_hi);
-    }
+  for (size_t l = 0; l < t.lanes.size(); ++l) {
+    gemm(t.lanes[l].o_gram, t.lanes[l].n_gram, 0, (int)l);
+    gemm(t.lanes[l].o_poly, t.lanes[l].n_poly, 1, (int)l);
+    gemm(t.lanes[l].o_upd, t.lanes[l].n_upd, 2, (int)l);
+  }
+  for (auto& kv : ksum[0]) CHECK(kv.second == ((int64_t)d[std::get<0>(kv.first)].n + 63) / 64);
+  for (int kind = 1; kind < 3; ++kind)
+    for (auto& kv : ksum[kind]) CHECK(kv.second == 1);
+  int64_t want_poly = 0, want_gram = 0, want_upd = 0;
+  for (int i = 0; i < n; ++i) {
+    want_poly += (int64_t)(d[i].m_pad / SYM_BM) * (d[i].m_pad / SYM_BM + 1) / 2;
+    want_gram += (int64_t)(d[i].m_pad / GRAM_BM) * (d[i].m_pad / GRAM_BM + 1) / 2;
+    want_upd += (int64_t)(d[i].m_pad / UPD_ROWU + UPD_BM / UPD_ROWU - 1) / (UPD_BM / UPD_ROWU) * (d[i].n_pad / UPD_BN);
+  }
+  CHECK((int64_t)ksum[0].size() == want_gram && (int64_t)ksum[1].size() == want_poly &&
+        (int64_t)ksum[2].size() == want_upd);
 }
 
 static void check_pointers(const Plan& p, const std::vector<PtrRecord>& r) {
@@ -275,7 +306,7 @@ static void test_tables_of_many_shapes() {
       PlanCache cache(&ops);
       const auto r = records(s, 0x7f0000000000ull);
       Plan* p = nullptr;
-      CHECK(cache.prepare(MODE_STEP, s.data(), (int)s.size(), r, false, &p) == MUON_OK);
+      CHECK(cache.prepare(MODE_STEP, s.data(), (int)s.size(), 3, r, false, &p) == MUON_OK);
       if (!p) continue;
       check_tables(*p, s, cache.workspace_bytes());
       check_pointers(*p, r);
@@ -291,17 +322,17 @@ static void test_pointer_alternation_needs_no_rebuild() {
   const auto s = gpt2_block(12);
   const auto a = records(s, 0x7f0000000000ull), b = records(s, 0x7e0000000000ull);
   Plan* p = nullptr;
-  CHECK(cache.prepare(MODE_STEP, s.data(), (int)s.size(), a, false, &p) == MUON_OK);
+  CHECK(cache.prepare(MODE_STEP, s.data(), (int)s.size(), 3, a, false, &p) == MUON_OK);
   const CacheStats first = cache.stats;
   CHECK(first.plan_builds == 1 && first.uploads == 1 && first.syncs == 0 && first.ws_allocs == 1);
   CHECK(first.patch_calls == 2);  // 48 matrices, 40 per patch
   // the same pointers again: nothing but the launches
-  CHECK(cache.prepare(MODE_STEP, s.data(), (int)s.size(), a, false, &p) == MUON_OK);
+  CHECK(cache.prepare(MODE_STEP, s.data(), (int)s.size(), 3, a, false, &p) == MUON_OK);
   CHECK(cache.stats.patch_calls == first.patch_calls);
   for (int k = 0; k < 10; ++k) {
     const auto& r = (k % 2) ? a : b;
     Plan* q = nullptr;
-    CHECK(cache.prepare(MODE_STEP, s.data(), (int)s.size(), r, false, &q) == MUON_OK);
+    CHECK(cache.prepare(MODE_STEP, s.data(), (int)s.size(), 3, r, false, &q) == MUON_OK);
     CHECK(q == p);
     check_pointers(*q, r);
   }
@@ -312,7 +343,7 @@ static void test_pointer_alternation_needs_no_rebuild() {
   std::vector<uint16_t*> out(s.size(), reinterpret_cast<uint16_t*>(0x1000));
   std::vector<const uint16_t*> in(s.size(), reinterpret_cast<const uint16_t*>(0x2000));
   make_ptr_records(MODE_NS, s.data(), (int)s.size(), nullptr, nullptr, nullptr, out.data(), in.data(), &x);
-  CHECK(cache.prepare(MODE_NS, s.data(), (int)s.size(), x, false, &p) == MUON_OK);
+  CHECK(cache.prepare(MODE_NS, s.data(), (int)s.size(), 3, x, false, &p) == MUON_OK);
   CHECK(cache.stats.plan_builds == 2 && cache.stats.syncs == 0);
 }
 
@@ -324,25 +355,25 @@ static void test_eviction_and_capture() {
     const auto s0 = shapes_of({{64, 64}});
     const auto r0 = records(s0, 0x7f0000000000ull);
     Plan* p0 = nullptr;
-    CHECK(cache.prepare(MODE_STEP, s0.data(), 1, r0, true, &p0) == MUON_EINVAL);  // never seen: refused
+    CHECK(cache.prepare(MODE_STEP, s0.data(), 1, 3, r0, true, &p0) == MUON_EINVAL);  // never seen: refused
     CHECK(cache.stats.plan_builds == 0);
-    CHECK(cache.prepare(MODE_STEP, s0.data(), 1, r0, false, &p0) == MUON_OK);
+    CHECK(cache.prepare(MODE_STEP, s0.data(), 1, 3, r0, false, &p0) == MUON_OK);
     const int64_t before = cache.stats.patch_calls;
     Plan* pc = nullptr;
-    CHECK(cache.prepare(MODE_STEP, s0.data(), 1, r0, true, &pc) == MUON_OK);
+    CHECK(cache.prepare(MODE_STEP, s0.data(), 1, 3, r0, true, &pc) == MUON_OK);
     CHECK(pc == p0 && pc->captured);
     CHECK(cache.stats.patch_calls == before + 1);  // a capture always records the pointer write
     // eager calls on a captured plan always re-patch (a replay writes its own pointers)
-    CHECK(cache.prepare(MODE_STEP, s0.data(), 1, r0, false, &pc) == MUON_OK);
+    CHECK(cache.prepare(MODE_STEP, s0.data(), 1, 3, r0, false, &pc) == MUON_OK);
     CHECK(cache.stats.patch_calls == before + 2);
     // a larger set of shapes refused under capture (it would allocate)
     const auto big = gpt2_block(1);
     const auto rb = records(big, 0x7d0000000000ull);
     Plan* pb = nullptr;
-    CHECK(cache.prepare(MODE_STEP, big.data(), (int)big.size(), rb, true, &pb) == MUON_EINVAL);
+    CHECK(cache.prepare(MODE_STEP, big.data(), (int)big.size(), 3, rb, true, &pb) == MUON_EINVAL);
     // ... fine eagerly: the workspace grows, the captured plan keeps the old one
     char* old_ws = p0->ws;
-    CHECK(cache.prepare(MODE_STEP, big.data(), (int)big.size(), rb, false, &pb) == MUON_OK);
+    CHECK(cache.prepare(MODE_STEP, big.data(), (int)big.size(), 3, rb, false, &pb) == MUON_OK);
     CHECK(cache.stats.syncs == 1);
     CHECK(ops.live.count(old_ws) == 1);  // retired, not freed
     CHECK(p0->captured && p0->ws == old_ws);
@@ -351,12 +382,12 @@ static void test_eviction_and_capture() {
       const auto s = shapes_of({{32 + k, 48}});
       const auto r = records(s, 0x7c0000000000ull);
       Plan* q = nullptr;
-      CHECK(cache.prepare(MODE_STEP, s.data(), 1, r, false, &q) == MUON_OK);
+      CHECK(cache.prepare(MODE_STEP, s.data(), 1, 3, r, false, &q) == MUON_OK);
     }
     CHECK(cache.stats.evictions == 2);
     CHECK(cache.plan_count() == PlanCache::kMaxPlans + 1);
     Plan* again = nullptr;
-    CHECK(cache.prepare(MODE_STEP, s0.data(), 1, r0, false, &again) == MUON_OK);
+    CHECK(cache.prepare(MODE_STEP, s0.data(), 1, 3, r0, false, &again) == MUON_OK);
     CHECK(again->key == p0->key || again->ws != old_ws);
   }
   CHECK(ops.live.empty());
@@ -370,19 +401,57 @@ static void test_caller_workspace() {
   std::vector<char> mine(workspace_bytes_of(s.data(), (int)s.size()) - 256);
   CHECK(cache.set_workspace(mine.data(), mine.size()) == MUON_OK);
   Plan* p = nullptr;
-  CHECK(cache.prepare(MODE_STEP, s.data(), (int)s.size(), r, false, &p) == MUON_ENOMEM);
+  CHECK(cache.prepare(MODE_STEP, s.data(), (int)s.size(), 3, r, false, &p) == MUON_ENOMEM);
   std::vector<char> enough(workspace_bytes_of(s.data(), (int)s.size()));
   CHECK(cache.set_workspace(enough.data(), enough.size()) == MUON_OK);
-  CHECK(cache.prepare(MODE_STEP, s.data(), (int)s.size(), r, false, &p) == MUON_OK);
+  CHECK(cache.prepare(MODE_STEP, s.data(), (int)s.size(), 3, r, false, &p) == MUON_OK);
   CHECK(p->ws == enough.data());
   check_tables(*p, s, enough.size());
   cache.release_all();  // does not free the caller's workspace
   CHECK(ops.live.empty());
   ops.fail_alloc = true;
-  CHECK(cache.prepare(MODE_STEP, s.data(), (int)s.size(), r, false, &p) == MUON_ENOMEM);
+  CHECK(cache.prepare(MODE_STEP, s.data(), (int)s.size(), 3, r, false, &p) == MUON_ENOMEM);
+}
+
+// Lanes regroup the work but never change an item: the same tiles, K
+// ranges and partial-tile slots as with one lane.
+static void test_lanes_change_no_item() {
+  const std::vector<std::vector<muon_shape_t>> sets = {gpt2_block(12), gpt2_block(1),
+                                                       shapes_of({{50257, 768}, {768, 768}}),
+                                                       shapes_of({{64, 4100}, {512, 20000}, {20001, 300}, {77, 77}})};
+  for (const auto& s : sets) {
+    std::vector<char> ws(workspace_bytes_of(s.data(), (int)s.size()));
+    std::set<std::tuple<int, int, int, int, int, int, int>> items[5];
+    size_t lanes_seen[5] = {0, 0, 0, 0, 0};
+    for (int L = 1; L <= kMaxLanes; ++L) {
+      PlanTables t;
+      CHECK(build_tables(MODE_STEP, s.data(), (int)s.size(), ws.data(), L, &t) == MUON_OK);
+      lanes_seen[L] = t.lanes.size();
+      std::set<std::tuple<int, int, int, int, int, int, int>> got;
+      for (const LaneTables& lt : t.lanes) {
+        const size_t offs[3] = {lt.o_gram, lt.o_poly, lt.o_upd};
+        const int cnts[3] = {lt.n_gram, lt.n_poly, lt.n_upd};
+        for (int kind = 0; kind < 3; ++kind) {
+          const GemmItem* it = reinterpret_cast<const GemmItem*>(t.image.data() + offs[kind]);
+          for (int k = 0; k < cnts[kind]; ++k)
+            if (it[k].mat >= 0) got.insert({kind, it[k].mat, it[k].ti, it[k].tj, it[k].k0, it[k].kn, it[k].slot});
+        }
+      }
+      items[L] = got;
+      if (L > 1) CHECK(items[L] == items[1]);
+    }
+    CHECK(lanes_seen[1] == 1);
+  }
+  // the GPT-2-124M hidden set: three shape groups, three lanes (two with two)
+  const auto s = gpt2_block(12);
+  const std::vector<int> l3 = lane_of_matrices(s.data(), (int)s.size(), 3);
+  const std::vector<int> l2 = lane_of_matrices(s.data(), (int)s.size(), 2);
+  CHECK(*std::max_element(l3.begin(), l3.end()) == 2 && *std::max_element(l2.begin(), l2.end()) == 1);
+  CHECK(l3[2] == 0 && l3[3] == 0);  // 768 x 3072 and its transpose: the costliest group first
 }
 
 int main() {
+  test_lanes_change_no_item();
   test_validation();
   test_tables_of_many_shapes();
   test_pointer_alternation_needs_no_rebuild();

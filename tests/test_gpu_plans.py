@@ -134,3 +134,32 @@ def test_guard_bands_around_edge_shapes(margin):
         r = oracle_steps(m, 2)
         check_matrix(f"{s}", W[i], M[i], U[i], r, m["W"].astype(np.float64))
         assert bf16_to_np(U[i]).shape == s
+
+
+def test_lanes_give_bit_identical_results():
+    """The lanes only decide which stream a shape group's kernels run on:
+    two steps on one GPT-2 block (three shape groups) with 1, 2 and 3 lanes
+    give the same bits, and match the oracle."""
+    torch = torch_mod()
+    import optimizer_muon_step_amd as mu
+    mats = [wl.make_matrix("c2", i, 2) for i in range(4)]
+    outs = []
+    try:
+        for lanes in (1, 2, 3):
+            mu.muon_set_lanes(lanes)
+            W = [to_gpu(m["W"]) for m in mats]
+            M = [to_gpu(m["buf"]) for m in mats]
+            for step in range(2):
+                mu.muon_step(W, [to_gpu(m["grads"][step]) for m in mats], M, LR, BETA, 5, COEFFS)
+            torch.cuda.synchronize()
+            outs.append((W, M))
+    finally:
+        mu.muon_set_lanes(1)
+    for W, M in outs[1:]:
+        for a, b in zip(W + M, outs[0][0] + outs[0][1]):
+            assert torch.equal(a, b)
+    for i, m in enumerate(mats):
+        r = oracle_steps(m, 2)
+        check_matrix(f"lanes matrix {i}", outs[2][0][i], outs[2][1][i], None, r, m["W"].astype(np.float64))
+    with pytest.raises(mu.MuonError, match="EINVAL"):
+        mu.muon_set_lanes(5)
