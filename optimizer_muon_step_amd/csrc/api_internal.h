@@ -28,6 +28,7 @@ struct Tables {
   GemmItem *gram, *poly, *upd;
   RedItem* red;
   float* gram_part;
+  bool small;
   const LaneTables* t;
 };
 Tables tables_at(char* block, const PlanTables& t, int lane, char* ws);

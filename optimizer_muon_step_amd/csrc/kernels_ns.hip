@@ -7,16 +7,26 @@
 namespace muon {
 
 hipError_t launch_gemm(int kind, const MatDesc* d, const GemmItem* items, int n_items, int src,
-                       float ca, float cb, float cc, float* part, hipStream_t s) {
+                       float ca, float cb, float cc, float* part, bool small, hipStream_t s) {
   if (n_items == 0) return hipSuccess;
   switch (kind) {
     case GEMM_GRAM:
-      return launch_gemm_gram(d, items, n_items, src, part, s);
+      return launch_gemm_gram(d, items, n_items, src, part, small, s);
     case GEMM_POLY:
-      ns_gemm_kernel<GEMM_POLY, SYM_BM, SYM_BN, 2, 4, SYM_NSTAGE, SYM_BM, SYM_BK><<<n_items, 512, 0, s>>>(d, items, src, ca, cb, cc, n_items, part);
+      if (small)
+        ns_gemm_kernel<GEMM_POLY, SMALL_SYM, SMALL_SYM, 2, 2, SMALL_SYM_NSTAGE, SMALL_SYM, 64, false>
+            <<<n_items, 256, 0, s>>>(d, items, src, ca, cb, cc, n_items, part);
+      else
+        ns_gemm_kernel<GEMM_POLY, SYM_BM, SYM_BN, 2, 4, SYM_NSTAGE, SYM_BM, SYM_BK, false>
+            <<<n_items, 512, 0, s>>>(d, items, src, ca, cb, cc, n_items, part);
       break;
     default:
-      ns_gemm_kernel<GEMM_UPDATE, UPD_BM, UPD_BN, 2, 4, 2, UPD_ROWU, 64><<<n_items < UPD_BLOCKS ? n_items : UPD_BLOCKS, 512, 0, s>>>(d, items, src, ca, cb, cc, n_items, part);
+      if (small)
+        ns_gemm_kernel<GEMM_UPDATE, SMALL_UPD_BM, SMALL_UPD_BN, 2, 2, SMALL_UPD_NSTAGE, UPD_ROWU, 64, false>
+            <<<n_items, 256, 0, s>>>(d, items, src, ca, cb, cc, n_items, part);
+      else
+        ns_gemm_kernel<GEMM_UPDATE, UPD_BM, UPD_BN, 2, 4, 2, UPD_ROWU, 64, true>
+            <<<n_items < UPD_BLOCKS ? n_items : UPD_BLOCKS, 512, 0, s>>>(d, items, src, ca, cb, cc, n_items, part);
       break;
   }
   return hipGetLastError();

@@ -15,10 +15,11 @@ hipError_t launch_cast(const MatDesc* d, const EwItem* items, int n_items, float
                        hipStream_t s);
 hipError_t launch_apply(const MatDesc* d, const EwItem* items, int n_items, float lr, int src,
                         int write_w, hipStream_t s);
+// small: the small-tile kernels (SMALL_SYM, SMALL_UPD_BM x SMALL_UPD_BN).
 hipError_t launch_gemm(int kind, const MatDesc* d, const GemmItem* items, int n_items, int src,
-                       float ca, float cb, float cc, float* part, hipStream_t s);
+                       float ca, float cb, float cc, float* part, bool small, hipStream_t s);
 hipError_t launch_gemm_gram(const MatDesc* d, const GemmItem* items, int n_items, int src, float* part,
-                            hipStream_t s);
+                            bool small, hipStream_t s);
 hipError_t launch_gram_reduce(const MatDesc* d, const RedItem* items, int n_items, const float* part,
                               hipStream_t s);
 // Table maintenance: write pointer records into descriptors, or a chunk of a

@@ -54,6 +54,19 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(n));
 }
 
+// Wait until at most `after` K slices of PER transfers each (issued after the
+// one needed now) are in flight; `after` is below NSTAGE - 1.
+template <int PER, int NSTAGE>
+__device__ __forceinline__ void wait_slices(int after) {
+  if (NSTAGE > 7 && after >= 6) wait_vm_lgkm0<6 * PER>();
+  else if (NSTAGE > 6 && after == 5) wait_vm_lgkm0<5 * PER>();
+  else if (NSTAGE > 5 && after == 4) wait_vm_lgkm0<4 * PER>();
+  else if (NSTAGE > 4 && after == 3) wait_vm_lgkm0<3 * PER>();
+  else if (NSTAGE > 3 && after == 2) wait_vm_lgkm0<2 * PER>();
+  else if (NSTAGE > 2 && after == 1) wait_vm_lgkm0<PER>();
+  else wait_vm_lgkm0<0>();
+}
+
 // k-contiguous tile, K slice of BK elements: rows of 2 BK bytes.  A fragment
 // read has 16 lanes on 16 consecutive rows at one 16-byte chunk.  128-byte
 // rows (BK 64, 8 chunks): two rows share a 256-byte bank line, so XOR by
@@ -94,8 +107,10 @@ struct TileCarry {
   bool prev_full;  // the previous tile issued all of its copy-out stores
 };
 
-// One output tile: work item idx of the list (not a padding item).
-template <int KIND, int BM, int BN, int WAVES_M, int WAVES_N, int NSTAGE, int ROWU, int BK>
+// One output tile: work item idx of the list (not a padding item).  PERSIST:
+// the blocks of the launch are persistent and each walks several items (only
+// for UPDATE, which then prefetches across tiles).
+template <int KIND, int BM, int BN, int WAVES_M, int WAVES_N, int NSTAGE, int ROWU, int BK, bool PERSIST>
 __device__ __forceinline__ void ns_gemm_tile(const MatDesc* __restrict__ descs, const GemmItem* __restrict__ items,
                                              int n_items, int idx, int src, float ca, float cb, float cc,
                                              float* __restrict__ part, TileCarry& carry) {
@@ -114,19 +129,28 @@ __device__ __forceinline__ void ns_gemm_tile(const MatDesc* __restrict__ descs, 
   constexpr int RPI = 1024 / RB;    // k-contiguous rows per wave DMA instruction
   static_assert(A_INSTR >= 1 && B_INSTR >= 1 && A_INSTR * 16 * NT == A_BYTES && B_INSTR * 16 * NT == B_BYTES,
                 "tile does not split into whole DMA instructions");
-  static_assert(NSTAGE >= 2 && NSTAGE <= 4 && TM >= 1 && TN >= 1, "unsupported tile");
+  static_assert(NSTAGE >= 2 && NSTAGE <= 8 && TM >= 1 && TN >= 1, "unsupported tile");
+  static_assert((NSTAGE - 2) * (A_INSTR + B_INSTR) <= 63, "in-flight transfers beyond the wait counter");
+  static_assert(!PERSIST || KIND == GEMM_UPDATE, "only the update launch is persistent");
   static_assert(!NN || BK == 64, "the k-major X slice is read 64 rows at a time");
   static_assert(!NN || ((TN == 2 || TN == 4) && BM % 32 == 0 && BK % 32 == 0 && ROWU % 32 == 0),
                 "UPDATE tiling: 32-row blocks of the tile each inside one K slice");
   static_assert(NN || ROWU == BM, "symmetric tiles are addressed in units of their own size");
   static_assert(!NN || BN >= 128, "k-major swizzle needs 16 chunks per row");
-  // UPDATE blocks are persistent (one per CU, each walking its tiles) and
-  // fetch the next tile's first K slice into stage 0 while the current tile's
-  // epilogue runs, so the staged output tile lives past stage 0.
-  constexpr bool PF = NN;
+  // Persistent UPDATE blocks (one per CU, each walking its tiles) fetch the
+  // next tile's first K slice into stage 0 while the current tile's epilogue
+  // runs, so the staged output tile lives past stage 0.
+  constexpr bool PF = NN && PERSIST;
   static_assert(!PF || NSTAGE == 2, "cross-tile prefetch: the last slice of a tile sits in stage 1");
   constexpr int E_OFF = PF ? STAGE_BYTES : 0;  // byte offset of the staged output tile
-  constexpr int LDS_BYTES = (E_OFF + BM * BN * 2 > NSTAGE * STAGE_BYTES) ? E_OFF + BM * BN * 2 : NSTAGE * STAGE_BYTES;
+  // Staged output rows: BN bf16 values.  A power-of-two count of 16-byte
+  // chunks (at least 16) is laid out with an XOR swizzle; fewer chunks get a
+  // row pitch one chunk longer instead, which moves consecutive rows to
+  // other banks by itself.
+  constexpr int RCH = BN / 8;  // 16-byte chunks per staged row
+  constexpr bool E_SWZ = (RCH >= 16) && ((RCH & (RCH - 1)) == 0);
+  constexpr int ROWB = E_SWZ ? BN * 2 : BN * 2 + 16;  // staged row pitch in bytes
+  constexpr int LDS_BYTES = (E_OFF + BM * ROWB > NSTAGE * STAGE_BYTES) ? E_OFF + BM * ROWB : NSTAGE * STAGE_BYTES;
   __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
   // byte offsets of slice s's A and B operand buffers
   auto a_off = [](int s) { return (s % NSTAGE) * STAGE_BYTES; };
@@ -431,12 +455,10 @@ __device__ __forceinline__ void ns_gemm_tile(const MatDesc* __restrict__ descs, 
       // memory operations complete in order, so it has landed once at most
       // those stores remain
       if (carry.prev_full) wait_vm_lgkm0<NSTORE>(); else wait_vm_lgkm0<0>();
-    } else if (after >= 2 && NSTAGE >= 4) {
-      if (same_rows) wait_vm_lgkm0<2 * A_INSTR>(); else wait_vm_lgkm0<2 * LPW>();
-    } else if (after >= 1 && NSTAGE >= 3) {
-      if (same_rows) wait_vm_lgkm0<A_INSTR>(); else wait_vm_lgkm0<LPW>();
+    } else if (same_rows) {
+      wait_slices<A_INSTR, NSTAGE>(after);
     } else {
-      wait_vm_lgkm0<0>();
+      wait_slices<LPW, NSTAGE>(after);
     }
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -492,16 +514,14 @@ __device__ __forceinline__ void ns_gemm_tile(const MatDesc* __restrict__ descs, 
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   LDS_AS char* E = (LDS_AS char*)lds + E_OFF;
-  constexpr int ROWB = BN * 2;          // staged row bytes
-  constexpr int RCH = BN / 8;           // 16-byte chunks per staged row
   static_assert(KIND == GEMM_UPDATE || BM == BN, "symmetric tiles are square");
   static_assert(BM * ROWB <= LDS_BYTES, "staging does not fit");
-  static_assert(RCH >= 16, "staging swizzle needs 16 chunks per row");
+  static_assert(E_SWZ || (RCH & (RCH - 1)) == 0, "staged rows of a power-of-two chunk count");
   // Chunk swizzle of a staged row.  Copy-out reads 16 lanes along one row
   // (any XOR keeps them distinct); the transposing reads of the mirror put a
   // 32-lane half on 4 consecutive rows and 4 consecutive chunks, which the
   // XOR by 4 (r % 4) sends to 4 different 64-byte bank groups.
-  auto ech = [&](int r, int c) { return c ^ (4 * (r & 3)) ^ ((r >> 2) & 3); };
+  auto ech = [&](int r, int c) { return E_SWZ ? c ^ (4 * (r & 3)) ^ ((r >> 2) & 3) : c; };
   const bool diag = (KIND != GEMM_UPDATE) && (row0 == col0);
 #pragma unroll
   for (int mi = 0; mi < TM; ++mi) {
@@ -586,24 +606,24 @@ __device__ __forceinline__ void ns_gemm_tile(const MatDesc* __restrict__ descs, 
   }
 }
 
-template <int KIND, int BM, int BN, int WAVES_M, int WAVES_N, int NSTAGE, int ROWU, int BK>
+template <int KIND, int BM, int BN, int WAVES_M, int WAVES_N, int NSTAGE, int ROWU, int BK, bool PERSIST>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void ns_gemm_kernel(const MatDesc* __restrict__ descs,
                                                                         const GemmItem* __restrict__ items,
                                                                         int src, float ca, float cb, float cc, int n_items,
                                                                         float* __restrict__ part) {
   TileCarry carry{false, false};
-  if constexpr (KIND == GEMM_UPDATE) {
+  if constexpr (PERSIST) {
     // UPD_BLOCKS persistent blocks: block b takes items b, b + gridDim.x, ...,
     // all planned for XCD b % 8 (gridDim.x is a multiple of 8 or n_items)
     for (int idx = blockIdx.x; idx < n_items; idx += gridDim.x) {
       if (items[idx].mat < 0) continue;  // padding item of a shorter per-XCD run
-      ns_gemm_tile<KIND, BM, BN, WAVES_M, WAVES_N, NSTAGE, ROWU, BK>(descs, items, n_items, idx, src, ca, cb, cc, part,
-                                                                     carry);
+      ns_gemm_tile<KIND, BM, BN, WAVES_M, WAVES_N, NSTAGE, ROWU, BK, PERSIST>(descs, items, n_items, idx, src, ca, cb,
+                                                                              cc, part, carry);
     }
   } else {
     if (items[blockIdx.x].mat < 0) return;  // padding item of a shorter per-XCD run
-    ns_gemm_tile<KIND, BM, BN, WAVES_M, WAVES_N, NSTAGE, ROWU, BK>(descs, items, n_items, blockIdx.x, src, ca, cb, cc,
-                                                                   part, carry);
+    ns_gemm_tile<KIND, BM, BN, WAVES_M, WAVES_N, NSTAGE, ROWU, BK, PERSIST>(descs, items, n_items, blockIdx.x, src, ca,
+                                                                            cb, cc, part, carry);
   }
 }
 

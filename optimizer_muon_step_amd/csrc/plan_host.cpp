@@ -112,8 +112,23 @@ int64_t gram_tiles(const Geometry& g) {
 }
 int64_t gram_chunks(int64_t slices, int64_t chunk) { return (chunk && slices > chunk) ? (slices + chunk - 1) / chunk : 1; }
 
+}  // namespace
+
+bool small_call(const muon_shape_t* shapes, int n) {
+  int64_t tiles = 0;
+  for (int i = 0; i < n; ++i) {
+    const Geometry g = geometry_of(shapes[i]);
+    const int64_t row_units = g.m_pad / UPD_ROWU, step = UPD_BM / UPD_ROWU;
+    tiles += (row_units + step - 1) / step * (g.n_pad / UPD_BN);
+  }
+  return n > 0 && tiles <= SMALL_MAX_UPD_TILES;
+}
+
+namespace {
+
 GramSplit gram_split_of(const muon_shape_t* shapes, int n) {
   GramSplit sp;
+  if (small_call(shapes, n)) return sp;
   int64_t total = 0, longest = 0;
   for (int i = 0; i < n; ++i) {
     const Geometry g = geometry_of(shapes[i]);
@@ -369,10 +384,15 @@ int build_tables(int mode, const muon_shape_t* shapes, int n, char* ws_base, int
   // phases: upper-triangle tiles row by row), then spread over the XCDs.
   // Gram and poly tiles differ in size (256 and 128); a long-K Gram tile may
   // be cut into K chunks, each its own item, summed by the reduce pass.
+  // Tile shapes of the call: the small-tile kernels when the update tiles
+  // cannot fill the GPU.
+  T.small = small_call(shapes, n);
+  const int gram_bm = T.small ? SMALL_SYM : GRAM_BM, poly_bm = T.small ? SMALL_SYM : SYM_BM;
+  const int upd_bm = T.small ? SMALL_UPD_BM : UPD_BM, upd_bn = T.small ? SMALL_UPD_BN : UPD_BN;
   int32_t slot = 0;
   for (int i = 0; i < n; ++i) {
     Lists& li = lists[lane_of[i]];
-    const int tg = desc[i].m_pad / GRAM_BM, tm = desc[i].m_pad / SYM_BM, tn = desc[i].n_pad / UPD_BN;
+    const int tg = desc[i].m_pad / gram_bm, tm = desc[i].m_pad / poly_bm, tn = desc[i].n_pad / upd_bn;
     const int64_t ks = ((int64_t)desc[i].n + 63) / 64;                   // Gram K slices
     const int32_t kp = (int32_t)(((int64_t)desc[i].m + SYM_BK - 1) / SYM_BK);  // poly K slices
     const int32_t ku = (int32_t)(2 * (((int64_t)desc[i].m + 127) / 128));  // update: even, see the kernel
@@ -399,7 +419,7 @@ int build_tables(int mode, const muon_shape_t* shapes, int n, char* ws_base, int
     for (int ti = 0; ti < tm; ++ti)
       for (int tj = ti; tj < tm; ++tj) li.poly_seq.push_back({i, (int16_t)ti, (int16_t)tj, 0, kp, -1});
     for (int tj = 0; tj < tn; ++tj)
-      for (int ti = 0; ti < desc[i].m_pad / UPD_ROWU; ti += UPD_BM / UPD_ROWU) {
+      for (int ti = 0; ti < desc[i].m_pad / UPD_ROWU; ti += upd_bm / UPD_ROWU) {
         li.upd_seq.push_back({i, (int16_t)ti, (int16_t)tj, 0, ku, -1});
         li.upd_cost.push_back(ku);
       }

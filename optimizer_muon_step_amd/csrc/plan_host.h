@@ -70,7 +70,13 @@ struct PlanTables {
   int n_mat = 0;
   std::vector<LaneTables> lanes;
   size_t gram_part_off = 0;  // Gram partial tiles, offset in the workspace
+  bool small = false;        // small-tile kernels (small_call)
 };
+
+// A call is small when it has at most SMALL_MAX_UPD_TILES update tiles of
+// UPD_BM x UPD_BN: it then runs the small-tile kernels and never cuts Gram
+// tiles.
+bool small_call(const muon_shape_t* shapes, int n);
 
 // Lanes: matrices of one canonical shape always share a lane; shape groups
 // are spread over at most max_lanes lanes, largest Newton-Schulz cost first

@@ -21,6 +21,16 @@ constexpr int UPD_BLOCKS = 256;
 constexpr int NS_PAD_M = 256;              // multiple of GRAM_BM and SYM_BM
 constexpr int NS_PAD_N = 256;              // multiple of UPD_BN
 constexpr int NS_THREADS = 256;
+// Calls of at most SMALL_MAX_UPD_TILES update tiles (above) use small tiles
+// with deep rings instead: 64 x 64 Gram and poly tiles and 64 x 128 update
+// tiles, four waves each, K slices of 64, most of a tile's slices in flight
+// at once (SMALL_*_NSTAGE stages: 128 KB and 144 KB of LDS), one tile per
+// block.  Measured per step on single matrices: better up to 36 update tiles
+// (768 x 2304), about even at 48 to 96, worse at 144 (one GPT-2 block).
+constexpr int SMALL_MAX_UPD_TILES = 40;
+constexpr int SMALL_SYM = 64;
+constexpr int SMALL_UPD_BM = 64, SMALL_UPD_BN = 128;
+constexpr int SMALL_SYM_NSTAGE = 8, SMALL_UPD_NSTAGE = 6;
 // Row strides of X (n_pad + NS_LD_PAD) and of A / B (m_pad + NS_LD_PAD), in
 // elements: 128 bytes past a multiple of 512 bytes, so that the rows a tile
 // touches spread over the L2 channels instead of repeating a few of them.
@@ -70,7 +80,7 @@ struct GemmItem {
 // GRAM_SPLIT_MIN slices; each chunk writes an fp32 partial tile and the
 // reduce pass sums a tile's chunks in K order, rounds once to bf16 and
 // mirrors.
-constexpr int GRAM_SPLIT_MIN = 16;  // slices of 64
+constexpr int GRAM_SPLIT_MIN = 2;  // slices of 64
 constexpr int NS_CUS = 256;         // CUs of the device the split is sized for
 constexpr int RED_TILE = 64;        // reduce pass: 64x64 sub-tile per block
 

@@ -205,6 +205,9 @@ static void check_tables(const Plan& p, const std::vector<muon_shape_t>& s, size
   }
   // GEMM items: tiles inside the padded matrix, K ranges inside the true
   // size, each output tile covered once per kind (Gram chunks tile K)
+  CHECK(t.small == small_call(s.data(), n));
+  const int gram_bm = t.small ? SMALL_SYM : GRAM_BM, poly_bm = t.small ? SMALL_SYM : SYM_BM;
+  const int upd_bm = t.small ? SMALL_UPD_BM : UPD_BM, upd_bn = t.small ? SMALL_UPD_BN : UPD_BN;
   std::map<std::tuple<int, int, int>, int64_t> ksum[3];
   auto gemm = [&](size_t off, int cnt, int kind, int lane) {
     const GemmItem* it = p.at<GemmItem>(off);
@@ -216,7 +219,8 @@ static void check_tables(const Plan& p, const std::vector<muon_shape_t>& s, size
       CHECK(lane_of[it[k].mat] == lane);
       const MatDesc& m = d[it[k].mat];
       if (kind == 0) {
-        CHECK(it[k].ti <= it[k].tj && (it[k].tj + 1) * GRAM_BM <= m.m_pad);
+        CHECK(it[k].ti <= it[k].tj && (it[k].tj + 1) * gram_bm <= m.m_pad);
+        CHECK(!t.small || it[k].slot < 0);
         CHECK(it[k].k0 >= 0 && (int64_t)(it[k].k0 + it[k].kn) * 64 <= m.n_pad && it[k].kn >= 1);
         ksum[0][{it[k].mat, it[k].ti, it[k].tj}] += it[k].kn;
         if (it[k].slot >= 0) {
@@ -224,13 +228,14 @@ static void check_tables(const Plan& p, const std::vector<muon_shape_t>& s, size
           CHECK(lo >= p.ws && lo + GRAM_BM * GRAM_BM * 4 <= ws_hi);
         }
       } else if (kind == 1) {
-        CHECK(it[k].ti <= it[k].tj && (it[k].tj + 1) * SYM_BM <= m.m_pad && it[k].kn * SYM_BK <= m.m_pad);
+        CHECK(it[k].ti <= it[k].tj && (it[k].tj + 1) * poly_bm <= m.m_pad && it[k].kn * SYM_BK <= m.m_pad);
         CHECK((int64_t)it[k].kn * SYM_BK >= m.m);
         ksum[1][{it[k].mat, it[k].ti, it[k].tj}] += 1;
       } else {
-        CHECK(it[k].ti * UPD_ROWU < m.m_pad && (it[k].tj + 1) * UPD_BN <= m.n_pad);
+        CHECK(it[k].ti * UPD_ROWU < m.m_pad && (it[k].tj + 1) * upd_bn <= m.n_pad);
+        CHECK(it[k].ti % (upd_bm / UPD_ROWU) == 0);
         CHECK(it[k].kn % 2 == 0 && it[k].kn * 64 <= m.m_pad);
-        CHECK(it[k].ti * UPD_ROWU + UPD_BM <= m.m_pad + NS_PAD_M);  // overhang inside the spare rows
+        CHECK(it[k].ti * UPD_ROWU + upd_bm <= m.m_pad + NS_PAD_M);  // overhang inside the spare rows
         ksum[2][{it[k].mat, it[k].ti, it[k].tj}] += 1;
       }
     }
@@ -245,9 +250,9 @@ static void check_tables(const Plan& p, const std::vector<muon_shape_t>& s, size
     for (auto& kv : ksum[kind]) CHECK(kv.second == 1);
   int64_t want_poly = 0, want_gram = 0, want_upd = 0;
   for (int i = 0; i < n; ++i) {
-    want_poly += (int64_t)(d[i].m_pad / SYM_BM) * (d[i].m_pad / SYM_BM + 1) / 2;
-    want_gram += (int64_t)(d[i].m_pad / GRAM_BM) * (d[i].m_pad / GRAM_BM + 1) / 2;
-    want_upd += (int64_t)(d[i].m_pad / UPD_ROWU + UPD_BM / UPD_ROWU - 1) / (UPD_BM / UPD_ROWU) * (d[i].n_pad / UPD_BN);
+    want_poly += (int64_t)(d[i].m_pad / poly_bm) * (d[i].m_pad / poly_bm + 1) / 2;
+    want_gram += (int64_t)(d[i].m_pad / gram_bm) * (d[i].m_pad / gram_bm + 1) / 2;
+    want_upd += (int64_t)(d[i].m_pad / UPD_ROWU + upd_bm / UPD_ROWU - 1) / (upd_bm / UPD_ROWU) * (d[i].n_pad / upd_bn);
   }
   CHECK((int64_t)ksum[0].size() == want_gram && (int64_t)ksum[1].size() == want_poly &&
         (int64_t)ksum[2].size() == want_upd);
@@ -448,6 +453,13 @@ static void test_lanes_change_no_item() {
   const std::vector<int> l2 = lane_of_matrices(s.data(), (int)s.size(), 2);
   CHECK(*std::max_element(l3.begin(), l3.end()) == 2 && *std::max_element(l2.begin(), l2.end()) == 1);
   CHECK(l3[2] == 0 && l3[3] == 0);  // 768 x 3072 and its transpose: the costliest group first
+  // small calls: one 256 x 512 matrix (4 update tiles), 768 x 2304 (36);
+  // not one GPT-2 block (144), 768 x 3072 (48), the hidden set (1728), the
+  // stress pair (800)
+  const auto c1 = shapes_of({{256, 512}}), c5 = shapes_of({{50257, 768}, {768, 768}});
+  const auto m36 = shapes_of({{768, 2304}}), m48 = shapes_of({{3072, 768}});
+  CHECK(small_call(c1.data(), 1) && small_call(m36.data(), 1) && !small_call(m48.data(), 1));
+  CHECK(!small_call(gpt2_block(1).data(), 4) && !small_call(s.data(), (int)s.size()) && !small_call(c5.data(), 2));
 }
 
 int main() {

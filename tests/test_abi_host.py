@@ -206,28 +206,43 @@ def test_workspace_bytes_host_logic(lib):
     assert one >= 2 * 768 * 2304 * 2 + 2 * 768 * 768 * 2
     assert ws([(2304, 768)]) - base == one  # orientation does not matter
     assert ws([(100, 200)]) - base >= 2 * 128 * 256 * 2 + 2 * 128 * 128 * 2
-    assert ws([(768, 2304), (768, 768)]) == base + one + (ws([(768, 768)]) - base)
+    # two small calls stay small together (16 update tiles): no Gram tile is cut
+    assert ws([(768, 768), (256, 512)]) == ws([(768, 768)]) + ws([(256, 512)]) - base
     assert lib.muon_workspace_bytes(_lib.shape_array([(0, 3)]), 1) == 0
     assert "shape" in lib.muon_last_error().decode()
 
 
 def test_workspace_bytes_long_k_gram_split(lib):
-    """A Gram tile whose K is more than twice the call's per-CU share is cut
-    into K chunks, one fp32 256x256 partial tile each: the only workspace
-    term that depends on the other matrices of the call."""
+    """In a call of more than 40 update tiles (192 x 256), a Gram tile whose K
+    is more than twice the call's per-CU share (total tile K slices / 256
+    CUs, at least 2) is cut into K chunks of about the share, one fp32
+    256x256 partial tile each: the only workspace term that depends on the
+    other matrices of the call.  Smaller calls run the small-tile kernels and
+    cut nothing."""
     def ws(shapes):
         return lib.muon_workspace_bytes(_lib.shape_array(shapes), len(shapes))
     base = ws([])
     part = 256 * 256 * 4
-    a = (256, 4096)    # one Gram tile of 64 K slices; alone the share is 16: 4 chunks
-    b = (2048, 2048)   # 36 tiles of 32 slices, never more than twice the share
-    alone = ws([a]) - base
-    b1 = ws([b]) - base
-    # with eight b the share is ceil((64 + 8 * 36 * 32) / 256) = 37: a is not cut
-    assert ws([a] + [b] * 8) - base == (alone - 4 * part) + 8 * b1
-    # with one b the share is ceil((64 + 1152) / 256) = 5 -> 16: a is cut in 4
-    # again, and b's 36 tiles, longer than the share, in 2 each
-    assert ws([a, b]) - base == alone + b1 + 36 * 2 * part
+    a = (256, 65536)   # one Gram tile of 1024 K slices; 512 update tiles
+    b = (2048, 2048)   # 36 Gram tiles of 32 slices; 88 update tiles
+    d = (64, 4100)     # one Gram tile of 65 slices; 34 update tiles: a small call alone
+    # a or d with eight b: share ceil((1024 + 8 * 1152) / 256) = 40 (a cut
+    # into ceil(1024 / 40) = 26 chunks, b's tiles of 32 <= 80 not cut) and
+    # ceil((65 + 9216) / 256) = 37 (d's 65 <= 74 not cut); eight b alone:
+    # share 36, nothing cut
+    core_a = ws([a] + [b] * 8) - ws([b] * 8) - 26 * part
+    core_d = ws([d] + [b] * 8) - ws([b] * 8)
+    core_b = (ws([b] * 8) - base) // 8
+    assert core_a > 2 * 256 * 65536 * 2 and core_b > 2 * 2048 * 2048 * 2
+    # a alone: share ceil(1024 / 256) = 4, so 1024 / 4 = 256 chunks
+    assert ws([a]) - base == core_a + 256 * part
+    # b alone: share ceil(1152 / 256) = 5; 32 > 10, so each tile in ceil(32 / 5) = 7
+    assert ws([b]) - base == core_b + 36 * 7 * part
+    # d alone is small: nothing cut (as a large call it would be cut in 33)
+    assert ws([d]) - base == core_d
+    # a with one b: share ceil((1024 + 1152) / 256) = 9: a in ceil(1024 / 9) =
+    # 114 chunks, each of b's 36 tiles in ceil(32 / 9) = 4
+    assert ws([a, b]) - base == core_a + core_b + (114 + 36 * 4) * part
 
 
 def test_timing_enable_validation(lib):

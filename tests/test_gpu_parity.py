@@ -98,11 +98,13 @@ def test_monomial_step_bit_exact(shape, transpose):
     assert np.array_equal(Wg[0].cpu().numpy(), r["W"])
 
 
-# Long-K Gram tiles cut into K chunks whose fp32 partials a reduce pass sums:
-# one diagonal tile (256 x 256 of a 64-row matrix), diagonal and off-diagonal
-# tiles of a 512-row matrix, and a ragged tall one; alone and mixed with
-# matrices whose tiles are not cut.
-@pytest.mark.parametrize("shape", [(64, 4100), (512, 20000), (20001, 300)])
+# Long K.  Calls with at least as many update tiles as CUs cut long-K Gram
+# tiles into K chunks whose fp32 partials a reduce pass sums: one diagonal
+# tile of 1024 slices (256 x 65536), diagonal and off-diagonal tiles of a
+# 1024-row matrix, and a ragged tall one.  Smaller calls (the first three
+# shapes) run the small-tile kernels, which walk the whole K in one tile.
+@pytest.mark.parametrize("shape", [(64, 4100), (512, 20000), (20001, 300), (256, 65536), (1024, 20000),
+                                   (20001, 600)])
 def test_newton_schulz_long_k_split(shape):
     import optimizer_muon_step_amd as mu
     say(f"[ns long K] shape={shape}")
@@ -121,7 +123,7 @@ def test_newton_schulz_long_k_split(shape):
 
 def test_newton_schulz_long_k_mixed_with_short():
     import optimizer_muon_step_amd as mu
-    shapes = [(512, 20000), (256, 256), (300, 200), (64, 2304)]
+    shapes = [(1024, 20000), (256, 256), (300, 200), (64, 2304)]
     bits = [_rand_bf16(s, 200 + i) for i, s in enumerate(shapes)]
     xs = [bf16_gpu(b) for b in bits]
     outs = [empty_bf16(s) for s in shapes]
