@@ -123,19 +123,19 @@ int muon_step_ex(float* const* params, const float* const* grads, float* const* 
  * graph capture, tight serving loops, harnesses that forbid allocation.
  * Same arguments, same kernels and bit-identical results as muon_step, but
  * the workspace and the plan tables live in a static device array of
- * MUON_NOALLOC_SCRATCH_BYTES (64 MiB) that every device the library runs on
+ * MUON_NOALLOC_SCRATCH_BYTES (128 MiB) that every device the library runs on
  * holds from the library's load until the process ends; no hipMalloc,
  * hipFree, pinned host memory or copy-engine transfer is used (the tables
  * and pointers reach the device as kernel arguments; host bookkeeping uses
  * the C++ heap).  A call whose workspace and tables exceed the array (one
- * GPT-2-124M block, 54.5 MiB, fits; the whole 48-matrix hidden set does not)
+ * GPT-2-124M block, 69.5 MiB, fits; the whole 48-matrix hidden set does not)
  * fails with MUON_ENOMEM and enqueues nothing.  Every call on a device
  * shares that device's array and leaves its contents behind; no call
  * depends on them (every value a kernel reads there was written earlier in
  * the same call), but calls whose GPU work overlaps in time on one device
  * race on the array: order them (one stream).
  */
-#define MUON_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+#define MUON_NOALLOC_SCRATCH_BYTES (128u * 1024u * 1024u)
 int muon_step_noalloc(float* const* params, const float* const* grads, float* const* momentum,
                       const muon_shape_t* shapes, int n, float lr, float beta, int ns_steps,
                       const float* coeffs, hipStream_t stream);

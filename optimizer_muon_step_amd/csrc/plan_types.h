@@ -80,7 +80,7 @@ struct GemmItem {
 // GRAM_SPLIT_MIN slices; each chunk writes an fp32 partial tile and the
 // reduce pass sums a tile's chunks in K order, rounds once to bf16 and
 // mirrors.
-constexpr int GRAM_SPLIT_MIN = 2;  // slices of 64
+constexpr int GRAM_SPLIT_MIN = 8;  // slices of 64
 constexpr int NS_CUS = 256;         // CUs of the device the split is sized for
 constexpr int RED_TILE = 64;        // reduce pass: 64x64 sub-tile per block
 

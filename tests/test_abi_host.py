@@ -215,7 +215,7 @@ def test_workspace_bytes_host_logic(lib):
 def test_workspace_bytes_long_k_gram_split(lib):
     """In a call of more than 40 update tiles (192 x 256), a Gram tile whose K
     is more than twice the call's per-CU share (total tile K slices / 256
-    CUs, at least 2) is cut into K chunks of about the share, one fp32
+    CUs, at least 8) is cut into K chunks of about the share, one fp32
     256x256 partial tile each: the only workspace term that depends on the
     other matrices of the call.  Smaller calls run the small-tile kernels and
     cut nothing."""
@@ -234,11 +234,11 @@ def test_workspace_bytes_long_k_gram_split(lib):
     core_d = ws([d] + [b] * 8) - ws([b] * 8)
     core_b = (ws([b] * 8) - base) // 8
     assert core_a > 2 * 256 * 65536 * 2 and core_b > 2 * 2048 * 2048 * 2
-    # a alone: share ceil(1024 / 256) = 4, so 1024 / 4 = 256 chunks
-    assert ws([a]) - base == core_a + 256 * part
-    # b alone: share ceil(1152 / 256) = 5; 32 > 10, so each tile in ceil(32 / 5) = 7
-    assert ws([b]) - base == core_b + 36 * 7 * part
-    # d alone is small: nothing cut (as a large call it would be cut in 33)
+    # a alone: share max(8, 1024 / 256) = 8, so 1024 / 8 = 128 chunks
+    assert ws([a]) - base == core_a + 128 * part
+    # b alone: share max(8, 1152 / 256) = 8; 32 > 16, so each tile in 32 / 8 = 4
+    assert ws([b]) - base == core_b + 36 * 4 * part
+    # d alone is small: nothing cut (as a large call it would be cut in 9)
     assert ws([d]) - base == core_d
     # a with one b: share ceil((1024 + 1152) / 256) = 9: a in ceil(1024 / 9) =
     # 114 chunks, each of b's 36 tiles in ceil(32 / 9) = 4
