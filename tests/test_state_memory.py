@@ -3,7 +3,12 @@ optimizer at half of AdamW's optimizer memory.  The state each step carries
 to the next is one fp32 momentum buffer per parameter for Muon (the
 momentum[] argument of muon_step) against two fp32 moments for AdamW
 (exp_avg[] and exp_avg_sq[] of muon_adamw_step).  Pinned by what the oracle
-steps return and by the byte count on the GPT-2-124M hidden set."""
+steps return and by the byte count on the GPT-2-124M hidden set.
+
+That is the state, not the library's footprint: muon_step also keeps a
+workspace across steps (bf16 iterates, A, B and norm partials), 513.1 MB on
+that set, so its device memory beyond the parameters (339.7 + 513.1 MB) is
+above AdamW's 679.5 MB of state.  The last test pins that figure."""
 import numpy as np
 
 from oracle import adamw_oracle as ao
@@ -35,3 +40,15 @@ def test_entry_points_take_that_state():
     # params, grads, exp_avg, exp_avg_sq (two state arrays)
     assert _lib.SIGNATURES["muon_step"][1][:3] == [_lib._PP] * 3
     assert _lib.SIGNATURES["muon_adamw_step"][1][:4] == [_lib._PP] * 4
+
+
+def test_workspace_beside_the_state():
+    """The workspace the step needs on the GPT-2-124M hidden set (host logic of
+    the library, no GPU): 513.1 MB, so state plus workspace exceed AdamW's
+    state there."""
+    shapes = [(s.rows, s.cols) for s in wl.config_specs("c3")]
+    import optimizer_muon_step_amd as mu
+    ws = mu.muon_workspace_bytes(shapes)
+    assert round(ws / 1e6, 1) == 513.1
+    n = sum(r * c for r, c in shapes)
+    assert n * 4 + ws > n * 8
