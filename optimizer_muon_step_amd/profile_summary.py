@@ -1,6 +1,6 @@
 """Summaries of rocprofv3 output for the committed profiles.
 
-Three subcommands, each reading the CSV files rocprofv3 writes with
+Four subcommands, each reading the CSV files rocprofv3 writes with
 `--output-format csv -o run`:
 
   trace   <dir> <out.md> --command CMD
@@ -19,6 +19,14 @@ Three subcommands, each reading the CSV files rocprofv3 writes with
       from one pass with SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_BF16,
       SQ_BUSY_CYCLES and GRBM_GUI_ACTIVE, with the kernel durations of a
       separate trace run beside it.
+
+  chain   <dir> <out.md> --group LABEL:SKIP:COUNT ... --command CMD
+      GPU-side anatomy of whole steps from <dir>/run_kernel_trace.csv: the
+      trace is cut into steps (a momentum launch up to the next apply launch,
+      in dispatch order); each group skips SKIP steps and summarises the next
+      COUNT: the step's span on the GPU (momentum start to apply end), the
+      time its kernels run, the idle time between them, the period from one
+      step's start to the next, and the mean duration of each kernel family.
 
 FETCH_SIZE and WRITE_SIZE count traffic between the L2 caches and the memory
 fabric, so reads served by the memory-side cache count as fetched.
@@ -41,6 +49,7 @@ FAMILIES = [
     (r"ns_gemm_kernel<0\b", "ns_gram"),
     (r"ns_gemm_kernel<1\b", "ns_poly"),
     (r"ns_gemm_kernel<2\b", "ns_update"),
+    (r"gram_reduce_kernel", "ns_gram_reduce"),
     (r"momentum_kernel", "momentum"),
     (r"norm_finalize_kernel", "norm_finalize"),
     (r"cast_kernel", "cast"),
@@ -48,6 +57,7 @@ FAMILIES = [
     (r"adamw_kernel", "adamw"),
     (r"untie_transpose_kernel", "untie"),
     (r"copyBuffer", "copy"),
+    (r"ptr_patch_kernel", "ptr_patch"),
 ]
 
 
@@ -244,6 +254,61 @@ def cmd_mfma(args):
     open(args.out, "w").write("\n".join(lines) + "\n")
 
 
+def cmd_chain(args):
+    rows = list(csv.DictReader(open(os.path.join(args.dir, "run_kernel_trace.csv"))))
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    steps, cur = [], None
+    for r in rows:
+        fam = family(r["Kernel_Name"])
+        if fam == "momentum":
+            cur = []
+        if cur is None:
+            continue
+        cur.append((fam, int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+        if fam == "apply":
+            steps.append(cur)
+            cur = None
+    lines = [f"# {args.title}", "", "Command (from the repository root on an MI355X):", "", "```", args.command, "```", ""]
+    if args.note:
+        lines += [args.note, ""]
+    lines += ["All times in microseconds, means over the steps of each group.  Span: first kernel start to last "
+              "kernel end of a step.  Busy: sum of its kernels' durations.  Idle: span minus busy, the time "
+              "between one kernel's end and the next one's start.  Period: one step's start to the next "
+              "step's start (the last step of a group has none).", "",
+              "| Workload | Steps | Launches per step | Span | Busy | Idle | Idle per launch | Period |",
+              "|:--|--:|--:|--:|--:|--:|--:|--:|"]
+    fam_tables = []
+    pos = 0
+    for g in args.group:
+        label, skip, count = g.split(":")
+        skip, count = int(skip), int(count)
+        sel = steps[pos + skip:pos + skip + count]
+        if len(sel) != count:
+            raise SystemExit(f"group {g}: only {len(sel)} steps left in the trace")
+        nxt = steps[pos + skip + 1:pos + skip + count + 1]
+        pos += skip + count
+        spans = [st[-1][2] - st[0][1] for st in sel]
+        busy = [sum(e - b for _, b, e in st) for st in sel]
+        periods = [n[0][1] - st[0][1] for st, n in zip(sel, nxt)][: count - 1]
+        launches = sum(len(st) for st in sel) / count
+        span, bsy = sum(spans) / count / 1e3, sum(busy) / count / 1e3
+        idle = span - bsy
+        period = sum(periods) / len(periods) / 1e3 if periods else float("nan")
+        lines.append(f"| {label} | {count} | {launches:.1f} | {span:.1f} | {bsy:.1f} | {idle:.1f} | "
+                     f"{idle / max(1.0, launches - 1):.2f} | {period:.1f} |")
+        per = collections.defaultdict(list)
+        for st in sel:
+            for fam, b, e in st:
+                per[fam].append((e - b) / 1e3)
+        fam_tables.append((label, count, per))
+    for label, count, per in fam_tables:
+        lines += ["", f"{label}: kernel families per step", "", "| Family | Launches per step | Mean (us) | Per step (us) |",
+                  "|:--|--:|--:|--:|"]
+        for fam, d in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+            lines.append(f"| {fam} | {len(d) / count:.1f} | {sum(d) / len(d):.2f} | {sum(d) / count:.1f} |")
+    open(args.out, "w").write("\n".join(lines) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -269,8 +334,15 @@ def main():
     m.add_argument("--command", required=True)
     m.add_argument("--title", default="Matrix-core use of the Newton-Schulz GEMMs")
     m.add_argument("--note", default="")
+    c = sub.add_parser("chain")
+    c.add_argument("dir")
+    c.add_argument("out")
+    c.add_argument("--group", action="append", required=True, help="LABEL:SKIP:COUNT, in trace order")
+    c.add_argument("--command", required=True)
+    c.add_argument("--title", default="Step anatomy on the GPU")
+    c.add_argument("--note", default="")
     args = ap.parse_args()
-    {"trace": cmd_trace, "traffic": cmd_traffic, "mfma": cmd_mfma}[args.cmd](args)
+    {"trace": cmd_trace, "traffic": cmd_traffic, "mfma": cmd_mfma, "chain": cmd_chain}[args.cmd](args)
 
 
 if __name__ == "__main__":
