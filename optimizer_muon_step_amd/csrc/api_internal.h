@@ -24,6 +24,7 @@ std::mutex& api_mutex();
 struct Tables {
   MatDesc* desc;
   int32_t* mats;
+  int32_t* fin;
   EwItem *mom, *cast, *apply;
   GemmItem *gram, *poly, *upd;
   RedItem* red;

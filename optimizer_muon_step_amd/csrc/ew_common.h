@@ -22,5 +22,30 @@ __device__ __forceinline__ float nesterov(float g, float m_new, float beta) {
   return g + beta * m_new;
 }
 
+// Fixed-order block sum of one double per thread; the total is valid in
+// thread 0.  Every thread of the block calls it.
+__device__ __forceinline__ double block_sum(double v, double* red) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  double s = 0.0;
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) s += red[w];
+  }
+  return s;
+}
+
+// s = 1 / (sqrt(sum of the matrix's norm partials) + 1e-7), valid in thread
+// 0.  The partials are summed in one fixed order (thread t takes partials t,
+// t + EW_THREADS, ..., then the block sum), whichever kernel calls it.
+__device__ __forceinline__ float norm_scale(const MatDesc& d, double* red) {
+  double v = 0.0;
+  for (int k = threadIdx.x; k < d.part_cnt; k += EW_THREADS) v += d.part[k];
+  v = block_sum(v, red);
+  return (float)(1.0 / (sqrt(v) + 1e-7));
+}
+
 }  // namespace ew
 }  // namespace muon

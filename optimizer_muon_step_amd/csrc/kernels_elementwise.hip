@@ -73,7 +73,21 @@ __global__ __launch_bounds__(EW_THREADS) void cast_kernel(const MatDesc* __restr
   const int tiles_j = d.n_pad / CAST_TILE;
   const int i0 = (it.idx / tiles_j) * CAST_TILE;
   const int j0 = (it.idx % tiles_j) * CAST_TILE;
-  const float s = FROM_BF16 ? 1.0f : *d.scale;
+  // the norm scale: summed here from the matrix's partials when it has few
+  // (the finalisation kernel's order, so the same bits), else its result
+  float s = 1.0f;
+  if (!FROM_BF16) {
+    if (d.part_cnt <= NORM_FOLD_MAX) {
+      __shared__ double red[kWaves];
+      __shared__ float s_fold;
+      const float f = norm_scale(d, red);
+      if (threadIdx.x == 0) s_fold = f;
+      __syncthreads();
+      s = s_fold;
+    } else {
+      s = *d.scale;
+    }
+  }
   MUON_GLOBAL uint16_t* X = gptr(d.X[0]);
   const int tc = (threadIdx.x & 15) * 4;
   const int tr = threadIdx.x >> 4;

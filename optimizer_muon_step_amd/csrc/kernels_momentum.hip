@@ -19,28 +19,12 @@ namespace muon {
 
 using namespace ew;
 
-namespace {
-
-// Fixed-order block sum of one double per thread; the total is valid in thread 0.
-__device__ double block_sum(double v, double* red) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  double s = 0.0;
-  if (threadIdx.x == 0) {
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) s += red[w];
-  }
-  return s;
-}
-
-}  // namespace
-
 // One work item = MOM_CHUNK consecutive elements of one matrix; it writes one
-// fp64 partial sum of U^2.  norm_finalize_kernel then reduces each matrix's
-// partials in index order, so the result does not depend on scheduling (and no
-// device-scope fence is needed inside the streaming kernel).  All loads of a
+// fp64 partial sum of U^2.  The partials of a matrix are then reduced in one
+// fixed order (norm_scale: by norm_finalize_kernel, or by each cast block for
+// matrices of at most NORM_FOLD_MAX partials), so the result does not depend
+// on scheduling (and no device-scope fence is needed inside the streaming
+// kernel).  All loads of a
 // batch are issued before any store so the whole batch is in flight at once.
 // G and M are read with non-temporal loads (measured 15% faster than cached
 // ones).  The new M is stored normally: the cast pass reads it again right
@@ -107,25 +91,23 @@ __global__ __launch_bounds__(EW_THREADS) void momentum_kernel(const MatDesc* __r
   if (threadIdx.x == 0) d.part[it.idx] = ss;
 }
 
-// One block per matrix of the list: s = 1 / (sqrt(sum of partials) + 1e-7),
-// the sum taken in a fixed order.
+// One block per matrix of the list (those with more than NORM_FOLD_MAX
+// partials): its scale s = 1 / (sqrt(sum of partials) + 1e-7).
 __global__ __launch_bounds__(EW_THREADS) void norm_finalize_kernel(const MatDesc* __restrict__ descs,
-                                                                   const int32_t* __restrict__ mats) {
+                                                                   const int32_t* __restrict__ fin) {
   __shared__ double red[kWaves];
-  const MatDesc& d = descs[mats[blockIdx.x]];
-  double v = 0.0;
-  for (int k = threadIdx.x; k < d.part_cnt; k += EW_THREADS) v += d.part[k];
-  v = block_sum(v, red);
-  if (threadIdx.x == 0) *d.scale = (float)(1.0 / (sqrt(v) + 1e-7));
+  const MatDesc& d = descs[fin[blockIdx.x]];
+  const float s = norm_scale(d, red);
+  if (threadIdx.x == 0) *d.scale = s;
 }
 
-hipError_t launch_momentum(const MatDesc* d, const EwItem* items, int n_items, const int32_t* mats, int n_mats,
+hipError_t launch_momentum(const MatDesc* d, const EwItem* items, int n_items, const int32_t* fin, int n_fin,
                            float beta, hipStream_t s) {
   if (n_items == 0) return hipSuccess;
   momentum_kernel<<<n_items, EW_THREADS, 0, s>>>(d, items, beta);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  norm_finalize_kernel<<<n_mats, EW_THREADS, 0, s>>>(d, mats);
+  if (e != hipSuccess || n_fin == 0) return e;
+  norm_finalize_kernel<<<n_fin, EW_THREADS, 0, s>>>(d, fin);
   return hipGetLastError();
 }
 

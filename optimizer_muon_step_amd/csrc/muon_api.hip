@@ -193,6 +193,7 @@ Tables tables_at(char* block, const PlanTables& t, int lane, char* ws) {
   Tables v;
   v.desc = reinterpret_cast<MatDesc*>(block + t.o_desc);
   v.mats = reinterpret_cast<int32_t*>(block + lt.o_mats);
+  v.fin = reinterpret_cast<int32_t*>(block + lt.o_fin);
   v.mom = reinterpret_cast<EwItem*>(block + lt.o_mom);
   v.cast = reinterpret_cast<EwItem*>(block + lt.o_cast);
   v.apply = reinterpret_cast<EwItem*>(block + lt.o_apply);
@@ -214,7 +215,7 @@ int launch_sequence(int mode, const Tables& v, float lr, float beta, int ns_step
   int rc;
   if (mode == MODE_STEP) {
     rc = timed(MUON_KERNEL_MOMENTUM, stream,
-               [&] { return launch_momentum(v.desc, v.mom, t.n_mom, v.mats, t.n_mats, beta, stream); },
+               [&] { return launch_momentum(v.desc, v.mom, t.n_mom, v.fin, t.n_fin, beta, stream); },
                "momentum kernel launch");
     if (rc) return rc;
   }

@@ -9,7 +9,7 @@
 namespace muon {
 
 // ---- host launchers (kernels_*.hip) ----
-hipError_t launch_momentum(const MatDesc* d, const EwItem* items, int n_items, const int32_t* mats, int n_mats,
+hipError_t launch_momentum(const MatDesc* d, const EwItem* items, int n_items, const int32_t* fin, int n_fin,
                            float beta, hipStream_t s);
 hipError_t launch_cast(const MatDesc* d, const EwItem* items, int n_items, float beta, int from_bf16,
                        hipStream_t s);

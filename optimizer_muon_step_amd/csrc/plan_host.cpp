@@ -330,7 +330,7 @@ int build_tables(int mode, const muon_shape_t* shapes, int n, char* ws_base, int
   const std::vector<int> lane_of = lane_of_matrices(shapes, n, max_lanes);
   const int L = n ? *std::max_element(lane_of.begin(), lane_of.end()) + 1 : 1;
   struct Lists {
-    std::vector<int32_t> mats;
+    std::vector<int32_t> mats, fin;
     std::vector<EwItem> mom, cast, apply;
     std::vector<GemmItem> gram_seq, poly_seq, upd_seq;
     std::vector<int64_t> gram_cost, upd_cost;
@@ -363,8 +363,10 @@ int build_tables(int mode, const muon_shape_t* shapes, int n, char* ws_base, int
     d.transposed = g.transposed;
     d.part_cnt = g.part_cnt;
     li.mats.push_back(i);
-    if (mode == MODE_STEP)
+    if (mode == MODE_STEP) {
       for (int c = 0; c < g.part_cnt; ++c) li.mom.push_back({i, c});
+      if (g.part_cnt > NORM_FOLD_MAX) li.fin.push_back(i);
+    }
     const int ct = (g.m_pad / CAST_TILE) * (g.n_pad / CAST_TILE);
     for (int t = 0; t < ct; ++t) li.cast.push_back({i, t});
     const int at = ((g.rows + CAST_TILE - 1) / CAST_TILE) * ((g.cols + CAST_TILE - 1) / CAST_TILE);
@@ -447,6 +449,7 @@ int build_tables(int mode, const muon_shape_t* shapes, int n, char* ws_base, int
     upd[l] = xcd_interleave(li.upd_seq, li.upd_cost);
     LaneTables& lt = T.lanes[l];
     lt.o_mats = place(sizeof(int32_t) * li.mats.size());
+    lt.o_fin = place(sizeof(int32_t) * li.fin.size());
     lt.o_mom = place(sizeof(EwItem) * li.mom.size());
     lt.o_cast = place(sizeof(EwItem) * li.cast.size());
     lt.o_apply = place(sizeof(EwItem) * li.apply.size());
@@ -455,6 +458,7 @@ int build_tables(int mode, const muon_shape_t* shapes, int n, char* ws_base, int
     lt.o_upd = place(sizeof(GemmItem) * upd[l].size());
     lt.o_red = place(sizeof(RedItem) * li.red.size());
     lt.n_mats = (int)li.mats.size();
+    lt.n_fin = (int)li.fin.size();
     lt.n_mom = (int)li.mom.size();
     lt.n_cast = (int)li.cast.size();
     lt.n_apply = (int)li.apply.size();
@@ -476,6 +480,7 @@ int build_tables(int mode, const muon_shape_t* shapes, int n, char* ws_base, int
     const Lists& li = lists[l];
     const LaneTables& lt = T.lanes[l];
     put(lt.o_mats, li.mats.data(), sizeof(int32_t) * li.mats.size());
+    put(lt.o_fin, li.fin.data(), sizeof(int32_t) * li.fin.size());
     put(lt.o_mom, li.mom.data(), sizeof(EwItem) * li.mom.size());
     put(lt.o_cast, li.cast.data(), sizeof(EwItem) * li.cast.size());
     put(lt.o_apply, li.apply.data(), sizeof(EwItem) * li.apply.size());

@@ -56,9 +56,11 @@ enum Mode { MODE_STEP = 0, MODE_NS = 1 };
 
 // Work lists of one lane: a group of matrices whose whole step runs as one
 // launch sequence (on a stream of its own when a call has several lanes).
+// fin: the matrices whose norm scale the finalisation kernel sums (more than
+// NORM_FOLD_MAX partials; the cast sums the others itself).
 struct LaneTables {
-  size_t o_mats = 0, o_mom = 0, o_cast = 0, o_apply = 0, o_gram = 0, o_poly = 0, o_upd = 0, o_red = 0;
-  int n_mats = 0, n_mom = 0, n_cast = 0, n_apply = 0, n_gram = 0, n_poly = 0, n_upd = 0, n_red = 0;
+  size_t o_mats = 0, o_fin = 0, o_mom = 0, o_cast = 0, o_apply = 0, o_gram = 0, o_poly = 0, o_upd = 0, o_red = 0;
+  int n_mats = 0, n_fin = 0, n_mom = 0, n_cast = 0, n_apply = 0, n_gram = 0, n_poly = 0, n_upd = 0, n_red = 0;
 };
 
 // Host image of a plan's device table block: descriptors (workspace pointers

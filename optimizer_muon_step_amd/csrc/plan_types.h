@@ -39,6 +39,10 @@ constexpr int NS_LD_PAD = 64;
 // Elementwise kernels.
 constexpr int EW_THREADS = 256;
 constexpr int MOM_CHUNK = 16384;  // elements per momentum work item (16 float4 per thread and array)
+// A matrix with at most NORM_FOLD_MAX norm partials has its scale summed by
+// every cast block itself, in the same fixed order as the finalisation
+// kernel (so to the same bits); only larger matrices take that launch.
+constexpr int NORM_FOLD_MAX = 256;
 constexpr int CAST_TILE = 64;     // square tile for the cast / apply kernels
 
 // One matrix of a call, in device memory.

@@ -173,6 +173,22 @@ static void check_tables(const Plan& p, const std::vector<muon_shape_t>& s, size
     n_cast += lt.n_cast;
     n_apply += lt.n_apply;
   }
+  // the finalisation list: in the step mode exactly the matrices with more
+  // than NORM_FOLD_MAX norm partials, each once, in its own lane
+  std::vector<int> fin_seen(n, 0);
+  for (size_t l = 0; l < t.lanes.size(); ++l) {
+    const LaneTables& lt = t.lanes[l];
+    const int32_t* fin = p.at<int32_t>(lt.o_fin);
+    for (int k = 0; k < lt.n_fin; ++k) {
+      CHECK(fin[k] >= 0 && fin[k] < n);
+      if (fin[k] < 0 || fin[k] >= n) continue;
+      CHECK(lane_of[fin[k]] == (int)l);
+      ++fin_seen[fin[k]];
+    }
+  }
+  const bool step_mode = !p.key.empty() && p.key[0] == MODE_STEP;
+  for (int i = 0; i < n; ++i)
+    CHECK(fin_seen[i] == ((step_mode && geometry_of(s[i]).part_cnt > NORM_FOLD_MAX) ? 1 : 0));
   for (int i = 0; i < n; ++i) {
     CHECK(lane_of[i] >= 0);
     for (int j = 0; j < n; ++j) {
