@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmuon.so")
 C_EXAMPLE = os.path.join(HERE, "muon_c_example")
 SOURCES = ["muon_api.hip", "muon_noalloc.hip", "plan_host.cpp", "kernels_tables.hip", "kernels_momentum.hip", "kernels_elementwise.hip",
-           "kernels_ns.hip", "kernels_ns_gram.hip", "kernels_adamw.hip"]
+           "kernels_ns.hip", "kernels_ns_gram.hip", "kernels_ns_fused.hip", "kernels_adamw.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -30,6 +30,7 @@ struct Tables {
   RedItem* red;
   float* gram_part;
   bool small;
+  bool fused;
   const LaneTables* t;
 };
 Tables tables_at(char* block, const PlanTables& t, int lane, char* ws);

@@ -203,6 +203,7 @@ Tables tables_at(char* block, const PlanTables& t, int lane, char* ws) {
   v.red = reinterpret_cast<RedItem*>(block + lt.o_red);
   v.gram_part = reinterpret_cast<float*>(ws + t.gram_part_off);
   v.small = t.small;
+  v.fused = t.fused;
   v.t = &lt;
   return v;
 }
@@ -233,6 +234,14 @@ int launch_sequence(int mode, const Tables& v, float lr, float beta, int ns_step
                },
                "gram kernel launch");
     if (rc) return rc;
+    if (v.fused) {
+      // poly and update in one launch (timed as the update)
+      rc = timed(MUON_KERNEL_UPDATE, stream,
+                 [&] { return launch_poly_update(v.desc, v.upd, t.n_upd, src, ca, cb, cc, stream); },
+                 "poly-update kernel launch");
+      if (rc) return rc;
+      continue;
+    }
     rc = timed(MUON_KERNEL_POLY, stream,
                [&] { return launch_gemm(GEMM_POLY, v.desc, v.poly, t.n_poly, src, ca, cb, cc, nullptr, v.small, stream); },
                "poly kernel launch");

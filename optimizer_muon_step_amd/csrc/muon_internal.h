@@ -20,6 +20,10 @@ hipError_t launch_gemm(int kind, const MatDesc* d, const GemmItem* items, int n_
                        float ca, float cb, float cc, float* part, bool small, hipStream_t s);
 hipError_t launch_gemm_gram(const MatDesc* d, const GemmItem* items, int n_items, int src, float* part,
                             bool small, hipStream_t s);
+// POLY and UPDATE of one iteration in one launch over the small update
+// tiles, for calls whose matrices all have m_pad = FUSED_M_PAD.
+hipError_t launch_poly_update(const MatDesc* d, const GemmItem* items, int n_items, int src, float ca, float cb,
+                              float cc, hipStream_t s);
 hipError_t launch_gram_reduce(const MatDesc* d, const RedItem* items, int n_items, const float* part,
                               hipStream_t s);
 // Table maintenance: write pointer records into descriptors, or a chunk of a

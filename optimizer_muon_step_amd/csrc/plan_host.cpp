@@ -389,6 +389,8 @@ int build_tables(int mode, const muon_shape_t* shapes, int n, char* ws_base, int
   // Tile shapes of the call: the small-tile kernels when the update tiles
   // cannot fill the GPU.
   T.small = small_call(shapes, n);
+  T.fused = T.small;
+  for (int i = 0; i < n; ++i) T.fused = T.fused && desc[i].m_pad == FUSED_M_PAD;
   const int gram_bm = T.small ? SMALL_SYM : GRAM_BM, poly_bm = T.small ? SMALL_SYM : SYM_BM;
   const int upd_bm = T.small ? SMALL_UPD_BM : UPD_BM, upd_bn = T.small ? SMALL_UPD_BN : UPD_BN;
   int32_t slot = 0;

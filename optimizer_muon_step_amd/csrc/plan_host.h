@@ -73,6 +73,7 @@ struct PlanTables {
   std::vector<LaneTables> lanes;
   size_t gram_part_off = 0;  // Gram partial tiles, offset in the workspace
   bool small = false;        // small-tile kernels (small_call)
+  bool fused = false;        // small, and every m_pad is 256: poly and update in one launch
 };
 
 // A call is small when it has at most SMALL_MAX_UPD_TILES update tiles of

@@ -31,6 +31,10 @@ constexpr int SMALL_MAX_UPD_TILES = 40;
 constexpr int SMALL_SYM = 64;
 constexpr int SMALL_UPD_BM = 64, SMALL_UPD_BN = 128;
 constexpr int SMALL_SYM_NSTAGE = 8, SMALL_UPD_NSTAGE = 6;
+// A small call whose matrices all have m_pad = FUSED_M_PAD (m <= 256) runs
+// poly and update as one launch per iteration (kernels_ns_fused.hip) over
+// the small update tiles.
+constexpr int FUSED_M_PAD = 256;
 // Row strides of X (n_pad + NS_LD_PAD) and of A / B (m_pad + NS_LD_PAD), in
 // elements: 128 bytes past a multiple of 512 bytes, so that the rows a tile
 // touches spread over the L2 channels instead of repeating a few of them.

@@ -222,6 +222,9 @@ static void check_tables(const Plan& p, const std::vector<muon_shape_t>& s, size
   // GEMM items: tiles inside the padded matrix, K ranges inside the true
   // size, each output tile covered once per kind (Gram chunks tile K)
   CHECK(t.small == small_call(s.data(), n));
+  bool fused = t.small;
+  for (int i = 0; i < n; ++i) fused = fused && geometry_of(s[i]).m_pad == FUSED_M_PAD;
+  CHECK(t.fused == fused);
   const int gram_bm = t.small ? SMALL_SYM : GRAM_BM, poly_bm = t.small ? SMALL_SYM : SYM_BM;
   const int upd_bm = t.small ? SMALL_UPD_BM : UPD_BM, upd_bn = t.small ? SMALL_UPD_BN : UPD_BN;
   std::map<std::tuple<int, int, int>, int64_t> ksum[3];
