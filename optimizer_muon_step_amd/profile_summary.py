@@ -50,6 +50,7 @@ FAMILIES = [
     (r"ns_gemm_kernel<1\b", "ns_poly"),
     (r"ns_gemm_kernel<2\b", "ns_update"),
     (r"gram_reduce_kernel", "ns_gram_reduce"),
+    (r"poly_update_kernel", "ns_poly_update"),
     (r"momentum_kernel", "momentum"),
     (r"norm_finalize_kernel", "norm_finalize"),
     (r"cast_kernel", "cast"),
