@@ -31,6 +31,7 @@ struct Tables {
   float* gram_part;
   bool small;
   bool fused;
+  int gram_tile, poly_tile, upd_tile, gram_bm;  // TileKind of each GEMM, Gram tile edge
   const LaneTables* t;
 };
 Tables tables_at(char* block, const PlanTables& t, int lane, char* ws);

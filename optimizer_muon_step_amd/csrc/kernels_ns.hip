@@ -7,13 +7,16 @@
 namespace muon {
 
 hipError_t launch_gemm(int kind, const MatDesc* d, const GemmItem* items, int n_items, int src,
-                       float ca, float cb, float cc, float* part, bool small, hipStream_t s) {
+                       float ca, float cb, float cc, float* part, int tile, hipStream_t s) {
   if (n_items == 0) return hipSuccess;
   switch (kind) {
     case GEMM_GRAM:
-      return launch_gemm_gram(d, items, n_items, src, part, small, s);
+      return launch_gemm_gram(d, items, n_items, src, part, tile, s);
     case GEMM_POLY:
-      if (small)
+      if (tile == TILE_MEDIUM)
+        ns_gemm_kernel<GEMM_POLY, MED_POLY_BM, MED_POLY_BM, 2, 2, MED_POLY_NSTAGE, MED_POLY_BM, 64, false>
+            <<<n_items, 256, 0, s>>>(d, items, src, ca, cb, cc, n_items, part);
+      else if (tile == TILE_SMALL)
         ns_gemm_kernel<GEMM_POLY, SMALL_SYM, SMALL_SYM, 2, 2, SMALL_SYM_NSTAGE, SMALL_SYM, 64, false>
             <<<n_items, 256, 0, s>>>(d, items, src, ca, cb, cc, n_items, part);
       else
@@ -21,7 +24,10 @@ hipError_t launch_gemm(int kind, const MatDesc* d, const GemmItem* items, int n_
             <<<n_items, 512, 0, s>>>(d, items, src, ca, cb, cc, n_items, part);
       break;
     default:
-      if (small)
+      if (tile == TILE_MEDIUM)
+        ns_gemm_kernel<GEMM_UPDATE, MED_UPD_BM, MED_UPD_BN, 2, 2, 2, UPD_ROWU, 64, false>
+            <<<n_items, 256, 0, s>>>(d, items, src, ca, cb, cc, n_items, part);
+      else if (tile == TILE_SMALL)
         ns_gemm_kernel<GEMM_UPDATE, SMALL_UPD_BM, SMALL_UPD_BN, 2, 2, SMALL_UPD_NSTAGE, UPD_ROWU, 64, false>
             <<<n_items, 256, 0, s>>>(d, items, src, ca, cb, cc, n_items, part);
       else
@@ -32,27 +38,28 @@ hipError_t launch_gemm(int kind, const MatDesc* d, const GemmItem* items, int n_
   return hipGetLastError();
 }
 
-// Reduce pass of split Gram tiles: one block per 64x64 sub-tile.  Each
+// Reduce pass of split Gram tiles (bm x bm, GRAM_BM or MED_GRAM_BM): one
+// block per 64x64 sub-tile.  Each
 // element sums its tile's chunk partials in K order in fp32, is rounded once
 // to bf16, and is written at (r, c) and mirrored to (c, r); a diagonal tile
 // keeps the values on and above its diagonal, so A stays exactly symmetric.
 __global__ __launch_bounds__(256) void gram_reduce_kernel(const MatDesc* __restrict__ descs,
                                                           const RedItem* __restrict__ items,
-                                                          const float* __restrict__ part) {
+                                                          const float* __restrict__ part, int bm) {
   constexpr int T = RED_TILE;
   __shared__ uint16_t tile[T][T + 2];
   const RedItem it = items[blockIdx.x];
   const MatDesc& d = descs[it.mat];
   MUON_GLOBAL uint16_t* A = gptr(d.A);
   const int ld = d.ld_a;
-  const int r0 = it.ti * GRAM_BM + it.bi * T, c0 = it.tj * GRAM_BM + it.bj * T;  // of A
+  const int r0 = it.ti * bm + it.bi * T, c0 = it.tj * bm + it.bj * T;  // of A
   const int i = threadIdx.x >> 2, j0 = (threadIdx.x & 3) * 16;                    // within the sub-tile
-  const float* src = part + (size_t)it.slot0 * (GRAM_BM * GRAM_BM) + (it.bi * T + i) * GRAM_BM + it.bj * T + j0;
+  const float* src = part + (size_t)it.slot0 * (bm * bm) + (it.bi * T + i) * bm + it.bj * T + j0;
   float v[16];
 #pragma unroll
   for (int k = 0; k < 16; ++k) v[k] = 0.0f;
   for (int c = 0; c < it.nchunk; ++c) {
-    const float4* p = reinterpret_cast<const float4*>(src + (size_t)c * (GRAM_BM * GRAM_BM));
+    const float4* p = reinterpret_cast<const float4*>(src + (size_t)c * (bm * bm));
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const float4 t = p[q];
@@ -101,10 +108,10 @@ __global__ __launch_bounds__(256) void gram_reduce_kernel(const MatDesc* __restr
   }
 }
 
-hipError_t launch_gram_reduce(const MatDesc* d, const RedItem* items, int n_items, const float* part,
+hipError_t launch_gram_reduce(const MatDesc* d, const RedItem* items, int n_items, const float* part, int bm,
                               hipStream_t s) {
   if (n_items == 0) return hipSuccess;
-  gram_reduce_kernel<<<n_items, 256, 0, s>>>(d, items, part);
+  gram_reduce_kernel<<<n_items, 256, 0, s>>>(d, items, part, bm);
   return hipGetLastError();
 }
 

@@ -6,11 +6,14 @@
 namespace muon {
 
 hipError_t launch_gemm_gram(const MatDesc* d, const GemmItem* items, int n_items, int src, float* part,
-                            bool small, hipStream_t s) {
+                            int tile, hipStream_t s) {
   if (n_items == 0) return hipSuccess;
-  if (small)
+  if (tile == TILE_SMALL)
     ns_gemm_kernel<GEMM_GRAM, SMALL_SYM, SMALL_SYM, 2, 2, SMALL_SYM_NSTAGE, SMALL_SYM, 64, false>
         <<<n_items, 256, 0, s>>>(d, items, src, 0.0f, 0.0f, 0.0f, n_items, part);
+  else if (tile == TILE_MEDIUM)
+    ns_gemm_kernel<GEMM_GRAM, MED_GRAM_BM, MED_GRAM_BM, 2, 4, 2, MED_GRAM_BM, 64, false>
+        <<<n_items, 512, 0, s>>>(d, items, src, 0.0f, 0.0f, 0.0f, n_items, part);
   else
     ns_gemm_kernel<GEMM_GRAM, GRAM_BM, GRAM_BM, 2, 4, 2, GRAM_BM, 64, false>
         <<<n_items, 512, 0, s>>>(d, items, src, 0.0f, 0.0f, 0.0f, n_items, part);

@@ -204,6 +204,10 @@ Tables tables_at(char* block, const PlanTables& t, int lane, char* ws) {
   v.gram_part = reinterpret_cast<float*>(ws + t.gram_part_off);
   v.small = t.small;
   v.fused = t.fused;
+  v.gram_tile = t.gram_tile;
+  v.poly_tile = t.poly_tile;
+  v.upd_tile = t.upd_tile;
+  v.gram_bm = t.gram_bm;
   v.t = &lt;
   return v;
 }
@@ -229,8 +233,8 @@ int launch_sequence(int mode, const Tables& v, float lr, float beta, int ns_step
     const float ca = ck[0], cb = ck[1], cc = ck[2];
     rc = timed(MUON_KERNEL_GRAM, stream,
                [&] {
-                 const hipError_t e = launch_gemm(GEMM_GRAM, v.desc, v.gram, t.n_gram, src, ca, cb, cc, v.gram_part, v.small, stream);
-                 return e != hipSuccess ? e : launch_gram_reduce(v.desc, v.red, t.n_red, v.gram_part, stream);
+                 const hipError_t e = launch_gemm(GEMM_GRAM, v.desc, v.gram, t.n_gram, src, ca, cb, cc, v.gram_part, v.gram_tile, stream);
+                 return e != hipSuccess ? e : launch_gram_reduce(v.desc, v.red, t.n_red, v.gram_part, v.gram_bm, stream);
                },
                "gram kernel launch");
     if (rc) return rc;
@@ -243,11 +247,11 @@ int launch_sequence(int mode, const Tables& v, float lr, float beta, int ns_step
       continue;
     }
     rc = timed(MUON_KERNEL_POLY, stream,
-               [&] { return launch_gemm(GEMM_POLY, v.desc, v.poly, t.n_poly, src, ca, cb, cc, nullptr, v.small, stream); },
+               [&] { return launch_gemm(GEMM_POLY, v.desc, v.poly, t.n_poly, src, ca, cb, cc, nullptr, v.poly_tile, stream); },
                "poly kernel launch");
     if (rc) return rc;
     rc = timed(MUON_KERNEL_UPDATE, stream,
-               [&] { return launch_gemm(GEMM_UPDATE, v.desc, v.upd, t.n_upd, src, ca, cb, cc, nullptr, v.small, stream); },
+               [&] { return launch_gemm(GEMM_UPDATE, v.desc, v.upd, t.n_upd, src, ca, cb, cc, nullptr, v.upd_tile, stream); },
                "update kernel launch");
     if (rc) return rc;
   }

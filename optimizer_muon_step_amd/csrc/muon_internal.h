@@ -15,16 +15,17 @@ hipError_t launch_cast(const MatDesc* d, const EwItem* items, int n_items, float
                        hipStream_t s);
 hipError_t launch_apply(const MatDesc* d, const EwItem* items, int n_items, float lr, int src,
                         int write_w, hipStream_t s);
-// small: the small-tile kernels (SMALL_SYM, SMALL_UPD_BM x SMALL_UPD_BN).
+// tile: the TileKind of the launch (large, small or medium tiles).
 hipError_t launch_gemm(int kind, const MatDesc* d, const GemmItem* items, int n_items, int src,
-                       float ca, float cb, float cc, float* part, bool small, hipStream_t s);
+                       float ca, float cb, float cc, float* part, int tile, hipStream_t s);
 hipError_t launch_gemm_gram(const MatDesc* d, const GemmItem* items, int n_items, int src, float* part,
-                            bool small, hipStream_t s);
+                            int tile, hipStream_t s);
 // POLY and UPDATE of one iteration in one launch over the small update
 // tiles, for calls whose matrices all have m_pad = FUSED_M_PAD.
 hipError_t launch_poly_update(const MatDesc* d, const GemmItem* items, int n_items, int src, float ca, float cb,
                               float cc, hipStream_t s);
-hipError_t launch_gram_reduce(const MatDesc* d, const RedItem* items, int n_items, const float* part,
+// bm: edge of the cut Gram tiles (and of their fp32 partial tiles).
+hipError_t launch_gram_reduce(const MatDesc* d, const RedItem* items, int n_items, const float* part, int bm,
                               hipStream_t s);
 // Table maintenance: write pointer records into descriptors, or a chunk of a
 // table image to device memory, in stream order (kernels_tables.hip).

@@ -106,33 +106,61 @@ struct GramSplit {
 
 // K slices of a Gram tile: the product runs to the true n (the padding is zero).
 int64_t gram_slices(const Geometry& g) { return ((int64_t)g.n + 63) / 64; }
-int64_t gram_tiles(const Geometry& g) {
-  const int64_t t = g.m_pad / GRAM_BM;
+int64_t gram_tiles(const Geometry& g, int bm) {
+  const int64_t t = g.m_pad / bm;
   return t * (t + 1) / 2;
 }
 int64_t gram_chunks(int64_t slices, int64_t chunk) { return (chunk && slices > chunk) ? (slices + chunk - 1) / chunk : 1; }
+
+// Update tiles of UPD_BM x UPD_BN (the last row tile may hang over m_pad).
+int64_t large_update_tiles(const Geometry& g) {
+  const int64_t row_units = g.m_pad / UPD_ROWU, step = UPD_BM / UPD_ROWU;
+  return (row_units + step - 1) / step * (g.n_pad / UPD_BN);
+}
 
 }  // namespace
 
 bool small_call(const muon_shape_t* shapes, int n) {
   int64_t tiles = 0;
+  for (int i = 0; i < n; ++i) tiles += large_update_tiles(geometry_of(shapes[i]));
+  return n > 0 && tiles <= SMALL_MAX_UPD_TILES;
+}
+
+TileChoice tile_choice(const muon_shape_t* shapes, int n) {
+  TileChoice c;
+  if (small_call(shapes, n)) {
+    c.gram = c.poly = c.upd = TILE_SMALL;
+    c.gram_bm = SMALL_SYM;
+    return c;
+  }
+  int64_t gram = 0, poly = 0, upd = 0, upd_med = 0;
   for (int i = 0; i < n; ++i) {
     const Geometry g = geometry_of(shapes[i]);
-    const int64_t row_units = g.m_pad / UPD_ROWU, step = UPD_BM / UPD_ROWU;
-    tiles += (row_units + step - 1) / step * (g.n_pad / UPD_BN);
+    gram += gram_tiles(g, GRAM_BM);
+    const int64_t t = g.m_pad / SYM_BM;
+    poly += t * (t + 1) / 2;
+    upd += large_update_tiles(g);
+    upd_med += (int64_t)(g.m_pad / MED_UPD_BM) * (g.n_pad / MED_UPD_BN);
   }
-  return n > 0 && tiles <= SMALL_MAX_UPD_TILES;
+  if (gram < NS_CUS) {
+    c.gram = TILE_MEDIUM;
+    c.gram_bm = MED_GRAM_BM;
+  }
+  if (poly <= MED_POLY_MAX_TILES) c.poly = TILE_MEDIUM;
+  if ((upd_med + 2 * NS_CUS - 1) / (2 * NS_CUS) <= (upd + NS_CUS - 1) / NS_CUS) c.upd = TILE_MEDIUM;
+  return c;
 }
 
 namespace {
 
 GramSplit gram_split_of(const muon_shape_t* shapes, int n) {
   GramSplit sp;
-  if (small_call(shapes, n)) return sp;
+  const TileChoice tc = tile_choice(shapes, n);
+  if (tc.gram == TILE_SMALL) return sp;
   int64_t total = 0, longest = 0;
   for (int i = 0; i < n; ++i) {
     const Geometry g = geometry_of(shapes[i]);
-    total += gram_tiles(g) * gram_slices(g);
+    total += gram_tiles(g, tc.gram_bm) * gram_slices(g);
     longest = std::max(longest, gram_slices(g));
   }
   const int64_t share = std::max<int64_t>(GRAM_SPLIT_MIN, (total + NS_CUS - 1) / NS_CUS);
@@ -141,7 +169,7 @@ GramSplit gram_split_of(const muon_shape_t* shapes, int n) {
   for (int i = 0; i < n; ++i) {
     const Geometry g = geometry_of(shapes[i]);
     const int64_t nc = gram_chunks(gram_slices(g), sp.chunk);
-    if (nc > 1) sp.slots += gram_tiles(g) * nc;
+    if (nc > 1) sp.slots += gram_tiles(g, tc.gram_bm) * nc;
   }
   return sp;
 }
@@ -291,7 +319,8 @@ size_t workspace_bytes_of(const muon_shape_t* shapes, int n) {
     const Geometry g = geometry_of(shapes[i]);
     total += 2 * g.x_bytes + 2 * g.a_bytes + g.part_bytes;
   }
-  total += align_up((size_t)gram_split_of(shapes, n).slots * GRAM_BM * GRAM_BM * sizeof(float));
+  const int bm = tile_choice(shapes, n).gram_bm;
+  total += align_up((size_t)gram_split_of(shapes, n).slots * bm * bm * sizeof(float));
   return total;
 }
 
@@ -379,20 +408,25 @@ int build_tables(int mode, const muon_shape_t* shapes, int n, char* ws_base, int
   // Partial tiles of split Gram tiles follow the matrices' buffers; the
   // split is decided over the whole call.
   const GramSplit split = gram_split_of(shapes, n);
+  const TileChoice tc = tile_choice(shapes, n);
   T.gram_part_off = (size_t)(cur - ws_base);
-  (void)carve<float>(cur, (size_t)split.slots * GRAM_BM * GRAM_BM);
+  (void)carve<float>(cur, (size_t)split.slots * tc.gram_bm * tc.gram_bm);
   // GEMM tiles.  Per matrix in an order that reuses operands (update: all row
   // tiles of one column block in a row, sharing that block of X; symmetric
   // phases: upper-triangle tiles row by row), then spread over the XCDs.
-  // Gram and poly tiles differ in size (256 and 128); a long-K Gram tile may
-  // be cut into K chunks, each its own item, summed by the reduce pass.
-  // Tile shapes of the call: the small-tile kernels when the update tiles
-  // cannot fill the GPU.
-  T.small = small_call(shapes, n);
+  // Each kind's tile shape comes from tile_choice; a long-K Gram tile may be
+  // cut into K chunks, each its own item, summed by the reduce pass.
+  T.small = tc.gram == TILE_SMALL;
   T.fused = T.small;
   for (int i = 0; i < n; ++i) T.fused = T.fused && desc[i].m_pad == FUSED_M_PAD;
-  const int gram_bm = T.small ? SMALL_SYM : GRAM_BM, poly_bm = T.small ? SMALL_SYM : SYM_BM;
-  const int upd_bm = T.small ? SMALL_UPD_BM : UPD_BM, upd_bn = T.small ? SMALL_UPD_BN : UPD_BN;
+  T.gram_tile = tc.gram;
+  T.poly_tile = tc.poly;
+  T.upd_tile = tc.upd;
+  T.gram_bm = tc.gram_bm;
+  const int gram_bm = tc.gram_bm;
+  const int poly_bm = tc.poly == TILE_SMALL ? SMALL_SYM : tc.poly == TILE_MEDIUM ? MED_POLY_BM : SYM_BM;
+  const int upd_bm = tc.upd == TILE_SMALL ? SMALL_UPD_BM : tc.upd == TILE_MEDIUM ? MED_UPD_BM : UPD_BM;
+  const int upd_bn = tc.upd == TILE_SMALL ? SMALL_UPD_BN : tc.upd == TILE_MEDIUM ? MED_UPD_BN : UPD_BN;
   int32_t slot = 0;
   for (int i = 0; i < n; ++i) {
     Lists& li = lists[lane_of[i]];
@@ -413,7 +447,7 @@ int build_tables(int mode, const muon_shape_t* shapes, int n, char* ws_base, int
           li.gram_seq.push_back({i, (int16_t)ti, (int16_t)tj, (int32_t)a, (int32_t)(b - a), slot + (int32_t)c});
           li.gram_cost.push_back(b - a);
         }
-        constexpr int SUB = GRAM_BM / RED_TILE;
+        const int SUB = gram_bm / RED_TILE;
         for (int bi = 0; bi < SUB; ++bi)
           for (int bj = 0; bj < SUB; ++bj)
             if (ti != tj || bi <= bj)

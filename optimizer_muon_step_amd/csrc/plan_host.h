@@ -74,12 +74,22 @@ struct PlanTables {
   size_t gram_part_off = 0;  // Gram partial tiles, offset in the workspace
   bool small = false;        // small-tile kernels (small_call)
   bool fused = false;        // small, and every m_pad is 256: poly and update in one launch
+  int gram_tile = TILE_LARGE, poly_tile = TILE_LARGE, upd_tile = TILE_LARGE;  // TileKind of each GEMM
+  int gram_bm = GRAM_BM;     // Gram tile edge (also of its partial tiles)
 };
 
 // A call is small when it has at most SMALL_MAX_UPD_TILES update tiles of
 // UPD_BM x UPD_BN: it then runs the small-tile kernels and never cuts Gram
 // tiles.
 bool small_call(const muon_shape_t* shapes, int n);
+
+// The tile kind of each GEMM of a call (TileKind; see plan_types.h) and the
+// Gram tile edge.
+struct TileChoice {
+  int gram = TILE_LARGE, poly = TILE_LARGE, upd = TILE_LARGE;
+  int gram_bm = GRAM_BM;
+};
+TileChoice tile_choice(const muon_shape_t* shapes, int n);
 
 // Lanes: matrices of one canonical shape always share a lane; shape groups
 // are spread over at most max_lanes lanes, largest Newton-Schulz cost first

@@ -31,6 +31,22 @@ constexpr int SMALL_MAX_UPD_TILES = 40;
 constexpr int SMALL_SYM = 64;
 constexpr int SMALL_UPD_BM = 64, SMALL_UPD_BN = 128;
 constexpr int SMALL_SYM_NSTAGE = 8, SMALL_UPD_NSTAGE = 6;
+// Tiles of a call that is not small, chosen per kernel kind from its tile
+// counts ("medium" tiles where the large ones would leave CUs idle):
+//   Gram    MED_GRAM_BM x MED_GRAM_BM (two blocks per CU) when the call has
+//           fewer Gram tiles of GRAM_BM than NS_CUS;
+//   poly    MED_POLY_BM x MED_POLY_BM with a MED_POLY_NSTAGE ring (two blocks
+//           per CU) when it has at most MED_POLY_MAX_TILES tiles of SYM_BM;
+//   update  MED_UPD_BM x MED_UPD_BN (two blocks per CU, not persistent) when
+//           those take no more rounds over 2 NS_CUS block slots than the
+//           UPD_BM x UPD_BN tiles take over NS_CUS persistent blocks.
+// Each output element accumulates its K in the same MFMA order whatever the
+// tile, so the choices change no bit, except where a Gram tile is cut.
+enum TileKind { TILE_LARGE = 0, TILE_SMALL = 1, TILE_MEDIUM = 2 };
+constexpr int MED_GRAM_BM = 128;
+constexpr int MED_POLY_BM = 64, MED_POLY_NSTAGE = 4, MED_POLY_MAX_TILES = 128;
+constexpr int MED_UPD_BM = 128, MED_UPD_BN = 128;
+
 // A small call whose matrices all have m_pad = FUSED_M_PAD (m <= 256) runs
 // poly and update as one launch per iteration (kernels_ns_fused.hip) over
 // the small update tiles.
@@ -95,7 +111,7 @@ constexpr int RED_TILE = 64;        // reduce pass: 64x64 sub-tile per block
 // Reduce work item: one 64x64 sub-tile of a split Gram tile.
 struct RedItem {
   int32_t mat;
-  int16_t ti, tj;    // Gram tile (units of GRAM_BM)
+  int16_t ti, tj;    // Gram tile (units of the call's Gram tile edge)
   int32_t slot0;     // first partial tile of its chunks
   int16_t nchunk;    // chunks, summed in order
   int8_t bi, bj;     // sub-tile within the Gram tile (units of RED_TILE)

@@ -225,8 +225,30 @@ static void check_tables(const Plan& p, const std::vector<muon_shape_t>& s, size
   bool fused = t.small;
   for (int i = 0; i < n; ++i) fused = fused && geometry_of(s[i]).m_pad == FUSED_M_PAD;
   CHECK(t.fused == fused);
-  const int gram_bm = t.small ? SMALL_SYM : GRAM_BM, poly_bm = t.small ? SMALL_SYM : SYM_BM;
-  const int upd_bm = t.small ? SMALL_UPD_BM : UPD_BM, upd_bn = t.small ? SMALL_UPD_BN : UPD_BN;
+  // tile kinds: all small in a small call, else each kind large or medium by
+  // its own tile count
+  {
+    int64_t g256 = 0, p128 = 0, u192 = 0, u128 = 0;
+    for (int i = 0; i < n; ++i) {
+      const Geometry g = geometry_of(s[i]);
+      g256 += (int64_t)(g.m_pad / 256) * (g.m_pad / 256 + 1) / 2;
+      p128 += (int64_t)(g.m_pad / 128) * (g.m_pad / 128 + 1) / 2;
+      u192 += (int64_t)((g.m_pad / 64 + 2) / 3) * (g.n_pad / 256);
+      u128 += (int64_t)(g.m_pad / 128) * (g.n_pad / 128);
+    }
+    if (t.small) {
+      CHECK(t.gram_tile == TILE_SMALL && t.poly_tile == TILE_SMALL && t.upd_tile == TILE_SMALL && t.gram_bm == 64);
+    } else {
+      CHECK(t.gram_tile == (g256 < 256 ? TILE_MEDIUM : TILE_LARGE));
+      CHECK(t.gram_bm == (g256 < 256 ? 128 : 256));
+      CHECK(t.poly_tile == (p128 <= 128 ? TILE_MEDIUM : TILE_LARGE));
+      CHECK(t.upd_tile == ((u128 + 511) / 512 <= (u192 + 255) / 256 ? TILE_MEDIUM : TILE_LARGE));
+    }
+  }
+  const int gram_bm = t.gram_bm;
+  const int poly_bm = t.poly_tile == TILE_SMALL ? 64 : t.poly_tile == TILE_MEDIUM ? 64 : 128;
+  const int upd_bm = t.upd_tile == TILE_SMALL ? 64 : t.upd_tile == TILE_MEDIUM ? 128 : 192;
+  const int upd_bn = t.upd_tile == TILE_LARGE ? 256 : 128;
   std::map<std::tuple<int, int, int>, int64_t> ksum[3];
   auto gemm = [&](size_t off, int cnt, int kind, int lane) {
     const GemmItem* it = p.at<GemmItem>(off);
@@ -243,8 +265,8 @@ static void check_tables(const Plan& p, const std::vector<muon_shape_t>& s, size
         CHECK(it[k].k0 >= 0 && (int64_t)(it[k].k0 + it[k].kn) * 64 <= m.n_pad && it[k].kn >= 1);
         ksum[0][{it[k].mat, it[k].ti, it[k].tj}] += it[k].kn;
         if (it[k].slot >= 0) {
-          const char* lo = p.ws + t.gram_part_off + (size_t)it[k].slot * GRAM_BM * GRAM_BM * 4;
-          CHECK(lo >= p.ws && lo + GRAM_BM * GRAM_BM * 4 <= ws_hi);
+          const char* lo = p.ws + t.gram_part_off + (size_t)it[k].slot * gram_bm * gram_bm * 4;
+          CHECK(lo >= p.ws && lo + (size_t)gram_bm * gram_bm * 4 <= ws_hi);
         }
       } else if (kind == 1) {
         CHECK(it[k].ti <= it[k].tj && (it[k].tj + 1) * poly_bm <= m.m_pad && it[k].kn * SYM_BK <= m.m_pad);

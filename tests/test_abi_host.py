@@ -213,36 +213,39 @@ def test_workspace_bytes_host_logic(lib):
 
 
 def test_workspace_bytes_long_k_gram_split(lib):
-    """In a call of more than 40 update tiles (192 x 256), a Gram tile whose K
-    is more than twice the call's per-CU share (total tile K slices / 256
-    CUs, at least 8) is cut into K chunks of about the share, one fp32
-    256x256 partial tile each: the only workspace term that depends on the
-    other matrices of the call.  Smaller calls run the small-tile kernels and
-    cut nothing."""
+    """In a call of more than 40 update tiles (192 x 256) whose longest Gram
+    tile K is more than twice the call's per-CU share (total tile K slices /
+    256 CUs, at least 8), every Gram tile longer than the share is cut into K
+    chunks of about the share, one fp32 partial tile each: the only workspace term that depends on the other
+    matrices of the call.  The Gram tiles are 256 x 256 in calls of at least
+    256 such tiles, else 128 x 128 (their partial tiles too).  Smaller calls
+    run the small-tile kernels and cut nothing."""
     def ws(shapes):
         return lib.muon_workspace_bytes(_lib.shape_array(shapes), len(shapes))
     base = ws([])
-    part = 256 * 256 * 4
-    a = (256, 65536)   # one Gram tile of 1024 K slices; 512 update tiles
-    b = (2048, 2048)   # 36 Gram tiles of 32 slices; 88 update tiles
+    part, part_med = 256 * 256 * 4, 128 * 128 * 4
+    a = (256, 65536)   # one Gram tile of 1024 K slices (three of 128); 512 update tiles
+    b = (2048, 2048)   # 36 Gram tiles of 32 slices (136 of 128); 88 update tiles
     d = (64, 4100)     # one Gram tile of 65 slices; 34 update tiles: a small call alone
-    # a or d with eight b: share ceil((1024 + 8 * 1152) / 256) = 40 (a cut
-    # into ceil(1024 / 40) = 26 chunks, b's tiles of 32 <= 80 not cut) and
-    # ceil((65 + 9216) / 256) = 37 (d's 65 <= 74 not cut); eight b alone:
-    # share 36, nothing cut
+    # a or d with eight b: 289 Gram tiles of 256, share ceil((1024 + 8 *
+    # 1152) / 256) = 40 (a cut into ceil(1024 / 40) = 26 chunks, b's tiles of
+    # 32 <= 80 not cut) and ceil((65 + 9216) / 256) = 37 (d's 65 <= 74 not
+    # cut); eight b alone: 288 tiles of 256, share 36, nothing cut
     core_a = ws([a] + [b] * 8) - ws([b] * 8) - 26 * part
     core_d = ws([d] + [b] * 8) - ws([b] * 8)
     core_b = (ws([b] * 8) - base) // 8
     assert core_a > 2 * 256 * 65536 * 2 and core_b > 2 * 2048 * 2048 * 2
-    # a alone: share max(8, 1024 / 256) = 8, so 1024 / 8 = 128 chunks
-    assert ws([a]) - base == core_a + 128 * part
-    # b alone: share max(8, 1152 / 256) = 8; 32 > 16, so each tile in 32 / 8 = 4
-    assert ws([b]) - base == core_b + 36 * 4 * part
-    # d alone is small: nothing cut (as a large call it would be cut in 9)
+    # a alone: three Gram tiles of 128, share max(8, 3072 / 256) = 12, each
+    # tile in ceil(1024 / 12) = 86 chunks
+    assert ws([a]) - base == core_a + 3 * 86 * part_med
+    # b alone: 136 tiles of 128, share ceil(4352 / 256) = 17; 32 <= 34, nothing cut
+    assert ws([b]) - base == core_b
+    # d alone is small: nothing cut
     assert ws([d]) - base == core_d
-    # a with one b: share ceil((1024 + 1152) / 256) = 9: a in ceil(1024 / 9) =
-    # 114 chunks, each of b's 36 tiles in ceil(32 / 9) = 4
-    assert ws([a, b]) - base == core_a + core_b + (114 + 36 * 4) * part
+    # a with one b: tiles of 128, share ceil((3072 + 4352) / 256) = 29, and
+    # a's 1024 > 58, so every tile longer than 29 is cut: each of a's in
+    # ceil(1024 / 29) = 36 chunks, each of b's 136 in ceil(32 / 29) = 2
+    assert ws([a, b]) - base == core_a + core_b + (3 * 36 + 136 * 2) * part_med
 
 
 def test_timing_enable_validation(lib):
