@@ -22,10 +22,14 @@ def _gpu():
     torch.cuda.synchronize()
 
 
-def test_captured_muon_step_replays_like_eager():
+# c1 runs the small tiles with poly and update in one launch, c2 the medium
+# tiles with cut Gram tiles and their reduce pass.
+@pytest.mark.parametrize("config,count", [("c1", 1), ("c2", 4)])
+def test_captured_muon_step_replays_like_eager(config, count):
     torch = torch_mod()
     import optimizer_muon_step_amd as mu
-    mats = [wl.make_matrix("c2", i, 4) for i in range(4)]
+    say(f"[graph] {config}")
+    mats = [wl.make_matrix(config, i, 4) for i in range(count)]
     W = [to_gpu(m["W"]) for m in mats]
     M = [to_gpu(m["buf"]) for m in mats]
     G = [to_gpu(m["grads"][0]) for m in mats]
