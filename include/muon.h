@@ -128,7 +128,7 @@ int muon_step_ex(float* const* params, const float* const* grads, float* const* 
  * hipFree, pinned host memory or copy-engine transfer is used (the tables
  * and pointers reach the device as kernel arguments; host bookkeeping uses
  * the C++ heap).  A call whose workspace and tables exceed the array (one
- * GPT-2-124M block, 69.5 MiB, fits; the whole 48-matrix hidden set does not)
+ * GPT-2-124M block, 55.4 MiB, fits; the whole 48-matrix hidden set does not)
  * fails with MUON_ENOMEM and enqueues nothing.  Every call on a device
  * shares that device's array and leaves its contents behind; no call
  * depends on them (every value a kernel reads there was written earlier in
