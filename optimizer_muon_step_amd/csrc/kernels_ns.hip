@@ -25,8 +25,8 @@ hipError_t launch_gemm(int kind, const MatDesc* d, const GemmItem* items, int n_
       break;
     default:
       if (tile == TILE_MEDIUM)
-        ns_gemm_kernel<GEMM_UPDATE, MED_UPD_BM, MED_UPD_BN, 2, 2, 2, UPD_ROWU, 64, false>
-            <<<n_items, 256, 0, s>>>(d, items, src, ca, cb, cc, n_items, part);
+        ns_gemm_kernel<GEMM_UPDATE, MED_UPD_BM, MED_UPD_BN, 2, 4, 2, UPD_ROWU, 64, false>
+            <<<n_items, 512, 0, s>>>(d, items, src, ca, cb, cc, n_items, part);
       else if (tile == TILE_SMALL)
         ns_gemm_kernel<GEMM_UPDATE, SMALL_UPD_BM, SMALL_UPD_BN, 2, 2, SMALL_UPD_NSTAGE, UPD_ROWU, 64, false>
             <<<n_items, 256, 0, s>>>(d, items, src, ca, cb, cc, n_items, part);

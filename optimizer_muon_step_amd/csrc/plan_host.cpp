@@ -147,7 +147,7 @@ TileChoice tile_choice(const muon_shape_t* shapes, int n) {
     c.gram_bm = MED_GRAM_BM;
   }
   if (poly <= MED_POLY_MAX_TILES) c.poly = TILE_MEDIUM;
-  if ((upd_med + 2 * NS_CUS - 1) / (2 * NS_CUS) <= (upd + NS_CUS - 1) / NS_CUS) c.upd = TILE_MEDIUM;
+  if ((upd_med + NS_CUS - 1) / NS_CUS <= (upd + NS_CUS - 1) / NS_CUS) c.upd = TILE_MEDIUM;
   return c;
 }
 

@@ -37,15 +37,15 @@ constexpr int SMALL_SYM_NSTAGE = 8, SMALL_UPD_NSTAGE = 6;
 //           fewer Gram tiles of GRAM_BM than NS_CUS;
 //   poly    MED_POLY_BM x MED_POLY_BM with a MED_POLY_NSTAGE ring (two blocks
 //           per CU) when it has at most MED_POLY_MAX_TILES tiles of SYM_BM;
-//   update  MED_UPD_BM x MED_UPD_BN (two blocks per CU, not persistent) when
-//           those take no more rounds over 2 NS_CUS block slots than the
-//           UPD_BM x UPD_BN tiles take over NS_CUS persistent blocks.
+//   update  MED_UPD_BM x MED_UPD_BN (one block per CU, not persistent) when
+//           those take no more rounds over NS_CUS CUs than the UPD_BM x
+//           UPD_BN tiles take over NS_CUS persistent blocks.
 // Each output element accumulates its K in the same MFMA order whatever the
 // tile, so the choices change no bit, except where a Gram tile is cut.
 enum TileKind { TILE_LARGE = 0, TILE_SMALL = 1, TILE_MEDIUM = 2 };
 constexpr int MED_GRAM_BM = 128;
 constexpr int MED_POLY_BM = 64, MED_POLY_NSTAGE = 4, MED_POLY_MAX_TILES = 128;
-constexpr int MED_UPD_BM = 128, MED_UPD_BN = 128;
+constexpr int MED_UPD_BM = 128, MED_UPD_BN = 256;
 
 // A small call whose matrices all have m_pad = FUSED_M_PAD (m <= 256) runs
 // poly and update as one launch per iteration (kernels_ns_fused.hip) over

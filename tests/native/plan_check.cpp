@@ -234,7 +234,7 @@ static void check_tables(const Plan& p, const std::vector<muon_shape_t>& s, size
       g256 += (int64_t)(g.m_pad / 256) * (g.m_pad / 256 + 1) / 2;
       p128 += (int64_t)(g.m_pad / 128) * (g.m_pad / 128 + 1) / 2;
       u192 += (int64_t)((g.m_pad / 64 + 2) / 3) * (g.n_pad / 256);
-      u128 += (int64_t)(g.m_pad / 128) * (g.n_pad / 128);
+      u128 += (int64_t)(g.m_pad / 128) * (g.n_pad / 256);
     }
     if (t.small) {
       CHECK(t.gram_tile == TILE_SMALL && t.poly_tile == TILE_SMALL && t.upd_tile == TILE_SMALL && t.gram_bm == 64);
@@ -242,13 +242,13 @@ static void check_tables(const Plan& p, const std::vector<muon_shape_t>& s, size
       CHECK(t.gram_tile == (g256 < 256 ? TILE_MEDIUM : TILE_LARGE));
       CHECK(t.gram_bm == (g256 < 256 ? 128 : 256));
       CHECK(t.poly_tile == (p128 <= 128 ? TILE_MEDIUM : TILE_LARGE));
-      CHECK(t.upd_tile == ((u128 + 511) / 512 <= (u192 + 255) / 256 ? TILE_MEDIUM : TILE_LARGE));
+      CHECK(t.upd_tile == ((u128 + 255) / 256 <= (u192 + 255) / 256 ? TILE_MEDIUM : TILE_LARGE));
     }
   }
   const int gram_bm = t.gram_bm;
   const int poly_bm = t.poly_tile == TILE_SMALL ? 64 : t.poly_tile == TILE_MEDIUM ? 64 : 128;
   const int upd_bm = t.upd_tile == TILE_SMALL ? 64 : t.upd_tile == TILE_MEDIUM ? 128 : 192;
-  const int upd_bn = t.upd_tile == TILE_LARGE ? 256 : 128;
+  const int upd_bn = t.upd_tile == TILE_SMALL ? 128 : 256;
   std::map<std::tuple<int, int, int>, int64_t> ksum[3];
   auto gemm = [&](size_t off, int cnt, int kind, int lane) {
     const GemmItem* it = p.at<GemmItem>(off);

@@ -44,7 +44,7 @@ def _ns_bits(bits):
 
 # Eight 2048 x 2048 matrices: 288 Gram tiles of 256 (large, K 32 within
 # twice the share of 36: not cut), 1088 poly tiles of 128 (large), 704
-# update tiles of 192 x 256 in 3 rounds against 2048 of 128 x 128 in 4
+# update tiles of 192 x 256 in 3 rounds against 1024 of 128 x 256 in 4
 # (large).
 COMPANIONS = [(2048, 2048)] * 8
 
@@ -52,11 +52,11 @@ COMPANIONS = [(2048, 2048)] * 8
 @pytest.mark.parametrize("shapes", [
     # Gram 128 x 128 (36 tiles of 256: fewer than the CUs; 136 of 128, K 32
     # within twice the share of 17), poly large (136 tiles of 128), update
-    # 128 x 128 (256 tiles, 1 round, against 88 of 192 x 256, 1 round)
+    # 128 x 256 (128 tiles, 1 round, against 88 of 192 x 256, 1 round)
     [(2048, 2048)],
     # every kind medium: Gram 108 tiles of 128 (K 16, share 8), poly 108
-    # tiles of 128 (at most 128: 64 x 64 tiles), update 192 tiles of 128 x
-    # 128 (1 round) against 72 of 192 x 256
+    # tiles of 128 (at most 128: 64 x 64 tiles), update 96 tiles of 128 x
+    # 256 (1 round) against 72 of 192 x 256
     [(1024, 1024)] * 3,
 ])
 def test_medium_tiles_match_large_tiles_bit_for_bit(shapes):
