@@ -25,8 +25,9 @@ constexpr int NS_THREADS = 256;
 // with deep rings instead: 64 x 64 Gram and poly tiles and 64 x 128 update
 // tiles, four waves each, K slices of 64, most of a tile's slices in flight
 // at once (SMALL_*_NSTAGE stages: 128 KB and 144 KB of LDS), one tile per
-// block.  Measured per step on single matrices: better up to 36 update tiles
-// (768 x 2304), about even at 48 to 96, worse at 144 (one GPT-2 block).
+// block.  Measured per step: better than the medium tiles below on calls of
+// up to 36 update tiles of square-ish matrices, slightly worse on long-K ones
+// at 36 (768 x 2304, 512 x 3072), far worse from 48 on.
 constexpr int SMALL_MAX_UPD_TILES = 40;
 constexpr int SMALL_SYM = 64;
 constexpr int SMALL_UPD_BM = 64, SMALL_UPD_BN = 128;
