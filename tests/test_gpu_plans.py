@@ -87,16 +87,25 @@ def _margins_intact(buf, margin, n, kind):
     return bool(np.all(host[:margin] == s) and np.all(host[margin + n:] == s))
 
 
+# Edge shapes (large update tiles, medium Gram and poly tiles), and a
+# mid-sized ragged set that takes the medium tiles for every kind.
+GUARD_SETS = {
+    "edge": [(50257, 768), (5, 4099), (257, 129), (129, 257), (1, 1), (300, 1)],
+    "medium": [(768, 3072), (3072, 769), (257, 1000)],
+}
+
+
 @pytest.mark.parametrize("margin", [4096, 4097])
-def test_guard_bands_around_edge_shapes(margin):
-    """Every W, G, momentum and update buffer of edge shapes sits between two
+@pytest.mark.parametrize("shape_set", sorted(GUARD_SETS))
+def test_guard_bands_around_edge_shapes(margin, shape_set):
+    """Every W, G, momentum and update buffer sits between two
     sentinel-filled margins; after two steps the margins are untouched and the
     results match the oracle.  margin 4097 also makes every array start off
     16-byte alignment (scalar paths)."""
     torch = torch_mod()
     import optimizer_muon_step_amd as mu
     rng = np.random.default_rng(70 + margin)
-    shapes = [(50257, 768), (5, 4099), (257, 129), (129, 257), (1, 1), (300, 1)]
+    shapes = GUARD_SETS[shape_set]
     say(f"[guard bands] margin {margin} elements, shapes {shapes}")
     mats = []
     for s in shapes:
