@@ -34,6 +34,16 @@ COEFFS = (3.4445, -4.7750, 2.0315)
 WORKLOAD = "c3"
 
 
+def ns_flops_dense(shapes):
+    """Flops of one Newton-Schulz iteration done as three dense GEMMs (no use
+    of symmetry): 2 m^2 n + 2 m^3 + 2 m^2 n per matrix."""
+    total = 0
+    for r, c in shapes:
+        m, n = min(r, c), max(r, c)
+        total += 4 * m * m * n + 2 * m * m * m
+    return total
+
+
 def ns_flops(shapes):
     """Algorithmic flops per launch of each Newton-Schulz GEMM, counting the
     symmetry of X X^T and of A A."""
@@ -438,8 +448,10 @@ def main():
         torch.cuda.synchronize()
         ns_ms = sum(breakdown[k]["ms_per_launch"] * breakdown[k]["launches_per_step"] for k in ("gram", "poly", "update"))
         ns_tf = ns_flops_step / (ns_ms * 1e-3) / 1e12
+        dense_tf = NS_STEPS * ns_flops_dense(shapes) / (ns_ms * 1e-3) / 1e12
         breakdown["ns_all"] = {"ms_per_step": round(ns_ms, 5), "TFLOP/s": round(ns_tf, 1),
-                               "frac_bf16_peak": round(ns_tf / PEAK_BF16_TFLOPS, 4)}
+                               "frac_bf16_peak": round(ns_tf / PEAK_BF16_TFLOPS, 4),
+                               "dense_equivalent_TFLOP/s": round(dense_tf, 1)}
 
     adamw = None if args.no_adamw else bench_adamw(torch, mu, wl)
     small = None if args.no_small else bench_small(torch, mu, wl)
