@@ -211,6 +211,26 @@ def test_ns_steps_zero_applies_x0():
     assert np.array_equal(Wg[0].cpu().numpy(), r["W"])
 
 
+@pytest.mark.parametrize("shapes", [[(2048, 2048), (2048, 2049), (4097, 1024)]])
+def test_norm_scale_on_both_sides_of_the_fold(shapes):
+    """A matrix of at most 256 norm partials (16384 elements each) has its
+    scale summed by every cast block, a larger one by the finalisation
+    launch; 2048 x 2048 has exactly 256, 2048 x 2049 and the tall 4097 x 1024
+    have 257.  With ns_steps = 0 the update is X0 = bf16(u * s), one rounding
+    of identical fp32 inputs with the same s, so both paths must match the
+    oracle bit for bit."""
+    rng = np.random.default_rng(11)
+    mats = [{"W": rng.standard_normal(s).astype(np.float32), "buf": (rng.standard_normal(s) * 1e-3).astype(np.float32),
+             "grads": [(rng.standard_normal(s) * 1e-3).astype(np.float32)]} for s in shapes]
+    say(f"[norm fold] {shapes}: {[-(-s[0] * s[1] // 16384) for s in shapes]} partials")
+    Wg, Mg, Ug = gpu_step(mats, "grads", 1, ns_steps=0)
+    for i, m in enumerate(mats):
+        r = oracle_steps(m, 1, ns_steps=0)
+        assert np.array_equal(Mg[i].cpu().numpy(), r["buf"])
+        assert np.array_equal(bf16_to_np(Ug[i]), r["O"]), f"{shapes[i]}"
+        assert np.array_equal(Wg[i].cpu().numpy(), r["W"]), f"{shapes[i]}"
+
+
 def test_zero_gradient_leaves_params():
     W = np.random.default_rng(6).standard_normal((64, 128)).astype(np.float32)
     m = {"W": W, "buf": np.zeros_like(W), "grads": [np.zeros_like(W)]}
