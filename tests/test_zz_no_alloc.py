@@ -66,6 +66,21 @@ def test_noalloc_matches_muon_step_on_two_calls_in_a_row():
             assert e <= NS_TOL
 
 
+def test_noalloc_on_the_small_fused_path():
+    """A call of small tiles with every m <= 256 (poly and update in one
+    launch), after the medium-tile calls above: bit-identical to muon_step."""
+    torch = torch_mod()
+    shapes = [(256, 512), (100, 300)]
+    mats = _inputs(shapes, 82)
+    ref = ([to_gpu(m["W"]) for m in mats], [to_gpu(m["grads"][0]) for m in mats], [to_gpu(m["buf"]) for m in mats])
+    got = ([to_gpu(m["W"]) for m in mats], [to_gpu(m["grads"][0]) for m in mats], [to_gpu(m["buf"]) for m in mats])
+    assert _call("muon_step", *ref) == 0, _lib.load().muon_last_error()
+    assert _call("muon_step_noalloc", *got) == 0, _lib.load().muon_last_error()
+    torch.cuda.synchronize()
+    for i, s in enumerate(shapes):
+        assert torch.equal(got[0][i], ref[0][i]) and torch.equal(got[2][i], ref[2][i]), f"{s} differs"
+
+
 def test_noalloc_refuses_calls_beyond_the_scratch():
     torch = torch_mod()
     shapes = [(s.rows, s.cols) for s in wl.config_specs("c3")]  # 489 MiB of workspace
