@@ -121,9 +121,13 @@ int64_t large_update_tiles(const Geometry& g) {
 }  // namespace
 
 bool small_call(const muon_shape_t* shapes, int n) {
-  int64_t tiles = 0;
-  for (int i = 0; i < n; ++i) tiles += large_update_tiles(geometry_of(shapes[i]));
-  return n > 0 && tiles <= SMALL_MAX_UPD_TILES;
+  int64_t tiles = 0, longest = 0;
+  for (int i = 0; i < n; ++i) {
+    const Geometry g = geometry_of(shapes[i]);
+    tiles += large_update_tiles(g);
+    longest = std::max(longest, gram_slices(g));
+  }
+  return n > 0 && tiles <= SMALL_MAX_UPD_TILES && longest <= SMALL_MAX_GRAM_SLICES;
 }
 
 TileChoice tile_choice(const muon_shape_t* shapes, int n) {

@@ -79,8 +79,8 @@ struct PlanTables {
 };
 
 // A call is small when it has at most SMALL_MAX_UPD_TILES update tiles of
-// UPD_BM x UPD_BN: it then runs the small-tile kernels and never cuts Gram
-// tiles.
+// UPD_BM x UPD_BN and no Gram K longer than SMALL_MAX_GRAM_SLICES slices: it
+// then runs the small-tile kernels and never cuts Gram tiles.
 bool small_call(const muon_shape_t* shapes, int n);
 
 // The tile kind of each GEMM of a call (TileKind; see plan_types.h) and the

@@ -25,10 +25,13 @@ constexpr int NS_THREADS = 256;
 // with deep rings instead: 64 x 64 Gram and poly tiles and 64 x 128 update
 // tiles, four waves each, K slices of 64, most of a tile's slices in flight
 // at once (SMALL_*_NSTAGE stages: 128 KB and 144 KB of LDS), one tile per
-// block.  Measured per step: better than the medium tiles below on calls of
-// up to 36 update tiles of square-ish matrices, slightly worse on long-K ones
-// at 36 (768 x 2304, 512 x 3072), far worse from 48 on.
+// block, and no Gram K cut, so a call with a Gram K of more than
+// SMALL_MAX_GRAM_SLICES slices of 64 (n > 2048) is not small: the medium
+// tiles below cut that K.  Measured per step: small tiles better than medium
+// ones on calls of up to 36 update tiles with n <= 1536, worse from n = 2048
+// on (256 x 4096 by 20 %) and on every call from 48 update tiles.
 constexpr int SMALL_MAX_UPD_TILES = 40;
+constexpr int SMALL_MAX_GRAM_SLICES = 32;
 constexpr int SMALL_SYM = 64;
 constexpr int SMALL_UPD_BM = 64, SMALL_UPD_BN = 128;
 constexpr int SMALL_SYM_NSTAGE = 8, SMALL_UPD_NSTAGE = 6;

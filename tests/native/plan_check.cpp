@@ -494,12 +494,15 @@ static void test_lanes_change_no_item() {
   const std::vector<int> l2 = lane_of_matrices(s.data(), (int)s.size(), 2);
   CHECK(*std::max_element(l3.begin(), l3.end()) == 2 && *std::max_element(l2.begin(), l2.end()) == 1);
   CHECK(l3[2] == 0 && l3[3] == 0);  // 768 x 3072 and its transpose: the costliest group first
-  // small calls: one 256 x 512 matrix (4 update tiles), 768 x 2304 (36);
-  // not one GPT-2 block (144), 768 x 3072 (48), the hidden set (1728), the
-  // stress pair (800)
+  // small calls: one 256 x 512 matrix (4 update tiles), 1024 x 1536 (36,
+  // Gram K 24 slices), 768 x 2048 (32, K 32); not 768 x 2304 (36 tiles but
+  // K 36 slices), 256 x 4096 (32 tiles, K 64), one GPT-2 block (144), 768 x
+  // 3072 (48), the hidden set (1728), the stress pair (800)
   const auto c1 = shapes_of({{256, 512}}), c5 = shapes_of({{50257, 768}, {768, 768}});
-  const auto m36 = shapes_of({{768, 2304}}), m48 = shapes_of({{3072, 768}});
-  CHECK(small_call(c1.data(), 1) && small_call(m36.data(), 1) && !small_call(m48.data(), 1));
+  const auto m36 = shapes_of({{1024, 1536}}), k32 = shapes_of({{768, 2048}}), m48 = shapes_of({{3072, 768}});
+  const auto k36 = shapes_of({{768, 2304}}), k64 = shapes_of({{256, 4096}});
+  CHECK(small_call(c1.data(), 1) && small_call(m36.data(), 1) && small_call(k32.data(), 1) && !small_call(m48.data(), 1));
+  CHECK(!small_call(k36.data(), 1) && !small_call(k64.data(), 1));
   CHECK(!small_call(gpt2_block(1).data(), 4) && !small_call(s.data(), (int)s.size()) && !small_call(c5.data(), 2));
 }
 

@@ -218,21 +218,24 @@ def test_workspace_bytes_long_k_gram_split(lib):
     256 CUs, at least 8), every Gram tile longer than the share is cut into K
     chunks of about the share, one fp32 partial tile each: the only workspace term that depends on the other
     matrices of the call.  The Gram tiles are 256 x 256 in calls of at least
-    256 such tiles, else 128 x 128 (their partial tiles too).  Smaller calls
-    run the small-tile kernels and cut nothing."""
+    256 such tiles, else 128 x 128 (their partial tiles too).  Calls of at
+    most 40 update tiles and no Gram K over 32 slices run the small-tile
+    kernels and cut nothing."""
     def ws(shapes):
         return lib.muon_workspace_bytes(_lib.shape_array(shapes), len(shapes))
     base = ws([])
     part, part_med = 256 * 256 * 4, 128 * 128 * 4
     a = (256, 65536)   # one Gram tile of 1024 K slices (three of 128); 512 update tiles
     b = (2048, 2048)   # 36 Gram tiles of 32 slices (136 of 128); 88 update tiles
-    d = (64, 4100)     # one Gram tile of 65 slices; 34 update tiles: a small call alone
+    d = (64, 4100)     # one Gram tile of 65 slices; 34 update tiles, but K over 32 slices: not small
+    e = (64, 2048)     # one Gram tile of 32 slices; 16 update tiles: a small call alone
     # a or d with eight b: 289 Gram tiles of 256, share ceil((1024 + 8 *
     # 1152) / 256) = 40 (a cut into ceil(1024 / 40) = 26 chunks, b's tiles of
     # 32 <= 80 not cut) and ceil((65 + 9216) / 256) = 37 (d's 65 <= 74 not
     # cut); eight b alone: 288 tiles of 256, share 36, nothing cut
     core_a = ws([a] + [b] * 8) - ws([b] * 8) - 26 * part
     core_d = ws([d] + [b] * 8) - ws([b] * 8)
+    core_e = ws([e] + [b] * 8) - ws([b] * 8)  # share 37: e's 32 slices not cut
     core_b = (ws([b] * 8) - base) // 8
     assert core_a > 2 * 256 * 65536 * 2 and core_b > 2 * 2048 * 2048 * 2
     # a alone: three Gram tiles of 128, share max(8, 3072 / 256) = 12, each
@@ -240,8 +243,10 @@ def test_workspace_bytes_long_k_gram_split(lib):
     assert ws([a]) - base == core_a + 3 * 86 * part_med
     # b alone: 136 tiles of 128, share ceil(4352 / 256) = 17; 32 <= 34, nothing cut
     assert ws([b]) - base == core_b
-    # d alone is small: nothing cut
-    assert ws([d]) - base == core_d
+    # d alone: three Gram tiles of 128, share 8, each in ceil(65 / 8) = 9 chunks
+    assert ws([d]) - base == core_d + 3 * 9 * part_med
+    # e alone is small: nothing cut
+    assert ws([e]) - base == core_e
     # a with one b: tiles of 128, share ceil((3072 + 4352) / 256) = 29, and
     # a's 1024 > 58, so every tile longer than 29 is cut: each of a's in
     # ceil(1024 / 29) = 36 chunks, each of b's 136 in ceil(32 / 29) = 2

@@ -98,11 +98,11 @@ def test_monomial_step_bit_exact(shape, transpose):
     assert np.array_equal(Wg[0].cpu().numpy(), r["W"])
 
 
-# Long K.  Calls with at least as many update tiles as CUs cut long-K Gram
-# tiles into K chunks whose fp32 partials a reduce pass sums: one diagonal
-# tile of 1024 slices (256 x 65536), diagonal and off-diagonal tiles of a
-# 1024-row matrix, and a ragged tall one.  Smaller calls (the first three
-# shapes) run the small-tile kernels, which walk the whole K in one tile.
+# Long K.  A call with a Gram K of more than 32 slices is not small, and
+# its long-K Gram tiles are cut into K chunks whose fp32 partials a reduce
+# pass sums: a single ragged tile row (64 x 4100), diagonal tiles of 1024
+# slices (256 x 65536), diagonal and off-diagonal tiles of a 1024-row
+# matrix, and ragged tall ones; each of these runs the 128-wide Gram tiles.
 @pytest.mark.parametrize("shape", [(64, 4100), (512, 20000), (20001, 300), (256, 65536), (1024, 20000),
                                    (20001, 600)])
 def test_newton_schulz_long_k_split(shape):
