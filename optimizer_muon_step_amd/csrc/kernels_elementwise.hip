@@ -68,7 +68,7 @@ __global__ __launch_bounds__(EW_THREADS) void cast_kernel(const MatDesc* __restr
                                                           const EwItem* __restrict__ items,
                                                           float beta) {
   __shared__ float T[CAST_TILE][CAST_TILE + 1];
-  const EwItem it = items[blockIdx.x];
+  const EwItem it = items[ew_item_of_block(blockIdx.x, gridDim.x, EW_TILE_RUN)];
   const MatDesc& d = descs[it.mat];
   const int tiles_j = d.n_pad / CAST_TILE;
   const int i0 = (it.idx / tiles_j) * CAST_TILE;
@@ -129,7 +129,7 @@ __global__ __launch_bounds__(EW_THREADS) void apply_kernel(const MatDesc* __rest
                                                            const EwItem* __restrict__ items, float lr,
                                                            int src, int write_w) {
   __shared__ uint16_t T[CAST_TILE][CAST_TILE + 2];
-  const EwItem it = items[blockIdx.x];
+  const EwItem it = items[ew_item_of_block(blockIdx.x, gridDim.x, EW_TILE_RUN)];
   const MatDesc& d = descs[it.mat];
   const int tiles_c = (d.cols + CAST_TILE - 1) / CAST_TILE;
   const int r0 = (it.idx / tiles_c) * CAST_TILE;

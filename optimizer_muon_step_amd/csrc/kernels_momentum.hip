@@ -35,7 +35,7 @@ __global__ __launch_bounds__(EW_THREADS) void momentum_kernel(const MatDesc* __r
                                                               float beta) {
   constexpr int V = MOM_CHUNK / (4 * EW_THREADS);  // float4 per thread
   __shared__ double red[kWaves];
-  const EwItem it = items[blockIdx.x];
+  const EwItem it = items[ew_item_of_block(blockIdx.x, gridDim.x, EW_MOM_RUN)];
   const MatDesc& d = descs[it.mat];
   const int64_t total = (int64_t)d.rows * d.cols;
   const int64_t base = (int64_t)it.idx * MOM_CHUNK;

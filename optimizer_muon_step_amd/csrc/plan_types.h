@@ -68,6 +68,25 @@ constexpr int MOM_CHUNK = 16384;  // elements per momentum work item (16 float4 
 // kernel (so to the same bits); only larger matrices take that launch.
 constexpr int NORM_FOLD_MAX = 256;
 constexpr int CAST_TILE = 64;     // square tile for the cast / apply kernels
+// Workgroups of a launch go to the 8 XCDs round-robin (workgroup b to XCD
+// b % 8).  The elementwise passes give each XCD runs of consecutive work
+// items in turn instead of every 8th item: XCD x takes items
+// 8Rg + xR .. 8Rg + xR + R - 1 of group g (a last, shorter group is split
+// into 8 near-equal runs), so fewer XCDs touch each page of the streamed
+// arrays while all of them stay inside one compact window of the list.
+// Measured per step (MI355X): c3 elementwise 440 -> 434 us, 192 GPT-2-XL
+// matrices 8.99 -> 8.46 ms; results do not depend on the map (every norm
+// partial is stored at its item's slot).
+constexpr int EW_MOM_RUN = 4;    // momentum items (MOM_CHUNK elements each)
+constexpr int EW_TILE_RUN = 16;  // cast / apply tiles
+constexpr int ew_item_of_block(int b, int nb, int run) {
+  const int group = 8 * run;
+  const int base = (b / group) * group;
+  const int t = (nb - base < group) ? nb - base : group;  // items of this group
+  const int w = b - base, x = w & 7, q = w >> 3;
+  const int full = t >> 3, rem = t & 7;
+  return base + x * full + (x < rem ? x : rem) + q;
+}
 
 // One matrix of a call, in device memory.
 struct MatDesc {

@@ -506,7 +506,35 @@ static void test_lanes_change_no_item() {
   CHECK(!small_call(gpt2_block(1).data(), 4) && !small_call(s.data(), (int)s.size()) && !small_call(c5.data(), 2));
 }
 
+// The elementwise passes' block -> item map: a permutation of the items for
+// any grid, the identity for runs of one, and in every whole group of 8R
+// blocks the blocks of one XCD (b % 8) take R consecutive items.
+static void test_elementwise_item_map() {
+  const int grids[] = {1, 5, 8, 9, 63, 64, 65, 431, 1000, 5184, 90001};
+  const int runs[] = {1, 2, EW_MOM_RUN, EW_TILE_RUN, 64};
+  for (int nb : grids)
+    for (int run : runs) {
+      std::vector<int> seen(nb, 0);
+      bool in_range = true;
+      for (int b = 0; b < nb; ++b) {
+        const int it = ew_item_of_block(b, nb, run);
+        if (it < 0 || it >= nb) { in_range = false; continue; }
+        ++seen[it];
+      }
+      CHECK(in_range);
+      CHECK(std::all_of(seen.begin(), seen.end(), [](int c) { return c == 1; }));
+      if (run == 1)
+        for (int b = 0; b < nb; ++b) CHECK(ew_item_of_block(b, nb, 1) == b);
+      const int group = 8 * run;
+      for (int b = 0; b + group <= nb && b < 4 * group; ++b) {
+        const int g = b / group, w = b % group;
+        CHECK(ew_item_of_block(b, nb, run) == g * group + (w % 8) * run + w / 8);
+      }
+    }
+}
+
 int main() {
+  test_elementwise_item_map();
   test_lanes_change_no_item();
   test_validation();
   test_tables_of_many_shapes();
