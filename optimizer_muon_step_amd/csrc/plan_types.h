@@ -42,8 +42,9 @@ constexpr int SMALL_SYM_NSTAGE = 8, SMALL_UPD_NSTAGE = 6;
 //   poly    MED_POLY_BM x MED_POLY_BM with a MED_POLY_NSTAGE ring (two blocks
 //           per CU) when it has at most MED_POLY_MAX_TILES tiles of SYM_BM;
 //   update  MED_UPD_BM x MED_UPD_BN (one block per CU, not persistent) when
-//           those take no more rounds over NS_CUS CUs than the UPD_BM x
-//           UPD_BN tiles take over NS_CUS persistent blocks.
+//           3 x their rounds over NS_CUS CUs is below 4 x the rounds of the
+//           UPD_BM x UPD_BN tiles over NS_CUS persistent blocks (a medium
+//           tile takes about three quarters of a large one's time).
 // Each output element accumulates its K in the same MFMA order whatever the
 // tile, so the choices change no bit, except where a Gram tile is cut.
 enum TileKind { TILE_LARGE = 0, TILE_SMALL = 1, TILE_MEDIUM = 2 };

@@ -242,7 +242,7 @@ static void check_tables(const Plan& p, const std::vector<muon_shape_t>& s, size
       CHECK(t.gram_tile == (g256 < 256 ? TILE_MEDIUM : TILE_LARGE));
       CHECK(t.gram_bm == (g256 < 256 ? 128 : 256));
       CHECK(t.poly_tile == (p128 <= 128 ? TILE_MEDIUM : TILE_LARGE));
-      CHECK(t.upd_tile == ((u128 + 255) / 256 <= (u192 + 255) / 256 ? TILE_MEDIUM : TILE_LARGE));
+      CHECK(t.upd_tile == (3 * ((u128 + 255) / 256) < 4 * ((u192 + 255) / 256) ? TILE_MEDIUM : TILE_LARGE));
     }
   }
   const int gram_bm = t.gram_bm;
@@ -533,8 +533,24 @@ static void test_elementwise_item_map() {
     }
 }
 
+// Update tiles of the named sets: the medium (128 x 256) tiles where their
+// rounds over the CUs cost less than the large tiles' (one GPT-2 block: 216
+// against 144 tiles, one round each; two blocks: 432 / 288, two rounds each;
+// the stress pair: 1200 / 800, five rounds against four), the large ones
+// where they do not (four blocks: 864 / 576, four rounds against three; the
+// hidden set: 2592 / 1728, eleven against seven).
+static void test_update_tile_choice() {
+  const auto c5 = shapes_of({{50257, 768}, {768, 768}});
+  CHECK(tile_choice(gpt2_block(1).data(), 4).upd == TILE_MEDIUM);
+  CHECK(tile_choice(gpt2_block(2).data(), 8).upd == TILE_MEDIUM);
+  CHECK(tile_choice(c5.data(), 2).upd == TILE_MEDIUM);
+  CHECK(tile_choice(gpt2_block(4).data(), 16).upd == TILE_LARGE);
+  CHECK(tile_choice(gpt2_block(12).data(), 48).upd == TILE_LARGE);
+}
+
 int main() {
   test_elementwise_item_map();
+  test_update_tile_choice();
   test_lanes_change_no_item();
   test_validation();
   test_tables_of_many_shapes();
