@@ -62,7 +62,8 @@ __device__ __forceinline__ void load4_src(const MatDesc& d, int r, int c, float 
   for (int k = 0; k < 4; ++k) out[k] = (c + k < d.cols) ? nesterov(g[k], m[k], beta) * s : 0.0f;
 }
 
-// One work item = one CAST_TILE x CAST_TILE tile of the canonical padded X0.
+// One work item = one CAST_TILE x CAST_TILE tile of the canonical padded X0
+// (blocks take the items in per-XCD runs of EW_TILE_RUN, ew_item_of_block).
 template <bool FROM_BF16>
 __global__ __launch_bounds__(EW_THREADS) void cast_kernel(const MatDesc* __restrict__ descs,
                                                           const EwItem* __restrict__ items,
@@ -124,7 +125,8 @@ __global__ __launch_bounds__(EW_THREADS) void cast_kernel(const MatDesc* __restr
   }
 }
 
-// One work item = one CAST_TILE x CAST_TILE tile of the caller's W.
+// One work item = one CAST_TILE x CAST_TILE tile of the caller's W (items in
+// per-XCD runs of EW_TILE_RUN, as in the cast).
 __global__ __launch_bounds__(EW_THREADS) void apply_kernel(const MatDesc* __restrict__ descs,
                                                            const EwItem* __restrict__ items, float lr,
                                                            int src, int write_w) {

@@ -19,8 +19,9 @@ namespace muon {
 
 using namespace ew;
 
-// One work item = MOM_CHUNK consecutive elements of one matrix; it writes one
-// fp64 partial sum of U^2.  The partials of a matrix are then reduced in one
+// One work item = MOM_CHUNK consecutive elements of one matrix (blocks take
+// the items in per-XCD runs of EW_MOM_RUN, ew_item_of_block); it writes one
+// fp64 partial sum of U^2, at the item's own slot.  The partials of a matrix are then reduced in one
 // fixed order (norm_scale: by norm_finalize_kernel, or by each cast block for
 // matrices of at most NORM_FOLD_MAX partials), so the result does not depend
 // on scheduling (and no device-scope fence is needed inside the streaming
