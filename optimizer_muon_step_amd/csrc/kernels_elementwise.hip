@@ -19,51 +19,47 @@ namespace muon {
 
 using namespace ew;
 
-// Value of canonical element (i, j) taken from source element (r, c); zero
-// outside the matrix.
-template <bool FROM_BF16>
-__device__ __forceinline__ void load4_src(const MatDesc& d, int r, int c, float beta, float s,
-                                          float out[4]) {
+// Four bf16 input elements (r, c .. c+3) of the Newton-Schulz-only entry as
+// fp32, zero outside the matrix.
+__device__ __forceinline__ void load4_xin(const MatDesc& d, int r, int c, float out[4]) {
   if (r >= d.rows) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) out[k] = 0.0f;
     return;
   }
   const int64_t off = (int64_t)r * d.cols + c;
-  if (FROM_BF16) {
-    if (d.vec4 && c + 3 < d.cols) {
-      const u32x2 w = *reinterpret_cast<const MUON_GLOBAL u32x2*>(gptr(d.xin) + off);
-      out[0] = bf16_lo(w.x);
-      out[1] = bf16_hi(w.x);
-      out[2] = bf16_lo(w.y);
-      out[3] = bf16_hi(w.y);
-    } else {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) out[k] = (c + k < d.cols) ? bf16_bits_to_f32(gptr(d.xin)[off + k]) : 0.0f;
-    }
-    return;
-  }
-  // G and M are read here for the last time in the step: non-temporal loads
-  float g[4], m[4];
   if (d.vec4 && c + 3 < d.cols) {
-    const f32x4 g4 = __builtin_nontemporal_load(reinterpret_cast<const MUON_GLOBAL f32x4*>(gptr(d.G) + off));
-    const f32x4 m4 = __builtin_nontemporal_load(reinterpret_cast<const MUON_GLOBAL f32x4*>(gptr(d.M) + off));
-    g[0] = g4.x; g[1] = g4.y; g[2] = g4.z; g[3] = g4.w;
-    m[0] = m4.x; m[1] = m4.y; m[2] = m4.z; m[3] = m4.w;
+    const u32x2 w = *reinterpret_cast<const MUON_GLOBAL u32x2*>(gptr(d.xin) + off);
+    out[0] = bf16_lo(w.x);
+    out[1] = bf16_hi(w.x);
+    out[2] = bf16_lo(w.y);
+    out[3] = bf16_hi(w.y);
   } else {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const bool in = c + k < d.cols;
-      g[k] = in ? gptr(d.G)[off + k] : 0.0f;
-      m[k] = in ? gptr(d.M)[off + k] : 0.0f;
-    }
+    for (int k = 0; k < 4; ++k) out[k] = (c + k < d.cols) ? bf16_bits_to_f32(gptr(d.xin)[off + k]) : 0.0f;
   }
-#pragma unroll
-  for (int k = 0; k < 4; ++k) out[k] = (c + k < d.cols) ? nesterov(g[k], m[k], beta) * s : 0.0f;
 }
 
-// One work item = one CAST_TILE x CAST_TILE tile of the canonical padded X0
-// (blocks take the items in per-XCD runs of EW_TILE_RUN, ew_item_of_block).
+// Four fp32 elements (r, c .. c+3) of G or M, zero outside the matrix; read
+// non-temporally (their last use in the step).
+__device__ __forceinline__ f32x4 load4_edge(const MUON_GLOBAL float* a, const MatDesc& d, int r, int c) {
+  f32x4 v = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  if (r >= d.rows) return v;
+  const int64_t off = (int64_t)r * d.cols + c;
+  if (d.vec4 && c + 3 < d.cols) return __builtin_nontemporal_load(reinterpret_cast<const MUON_GLOBAL f32x4*>(a + off));
+  v.x = c < d.cols ? a[off] : 0.0f;
+  v.y = c + 1 < d.cols ? a[off + 1] : 0.0f;
+  v.z = c + 2 < d.cols ? a[off + 2] : 0.0f;
+  v.w = c + 3 < d.cols ? a[off + 3] : 0.0f;
+  return v;
+}
+
+// One work item = one tile of the canonical padded X0 (blocks take the items
+// in per-XCD runs of EW_TILE_RUN, ew_item_of_block): CAST_WIDE_ROWS x
+// CAST_WIDE_COLS for an untransposed matrix, CAST_TILE x CAST_TILE staged
+// through LDS for a transposed one.  G and M go out first, eight 16-byte
+// loads per thread in one batch on interior tiles, and the norm scale is
+// taken while they are in flight.
 template <bool FROM_BF16>
 __global__ __launch_bounds__(EW_THREADS) void cast_kernel(const MatDesc* __restrict__ descs,
                                                           const EwItem* __restrict__ items,
@@ -71,52 +67,92 @@ __global__ __launch_bounds__(EW_THREADS) void cast_kernel(const MatDesc* __restr
   __shared__ float T[CAST_TILE][CAST_TILE + 1];
   const EwItem it = items[ew_item_of_block(blockIdx.x, gridDim.x, EW_TILE_RUN)];
   const MatDesc& d = descs[it.mat];
-  const int tiles_j = d.n_pad / CAST_TILE;
-  const int i0 = (it.idx / tiles_j) * CAST_TILE;
-  const int j0 = (it.idx % tiles_j) * CAST_TILE;
-  // the norm scale: summed here from the matrix's partials when it has few
-  // (the finalisation kernel's order, so the same bits), else its result
-  float s = 1.0f;
+  const bool trn = d.transposed;
+  // tile origin (i0, j0) in X0; this thread's source rows sr0 + tr + rstep q
+  // (q = 0..3), columns sc0 + tc .. +3
+  int i0, j0, tr, tc, rstep, srows, scols;
+  if (!trn) {
+    const int tiles_j = d.n_pad / CAST_WIDE_COLS;
+    i0 = (it.idx / tiles_j) * CAST_WIDE_ROWS;
+    j0 = (it.idx % tiles_j) * CAST_WIDE_COLS;
+    tc = (threadIdx.x % (CAST_WIDE_COLS / 4)) * 4;
+    tr = threadIdx.x / (CAST_WIDE_COLS / 4);
+    rstep = CAST_WIDE_ROWS / 4;
+    srows = CAST_WIDE_ROWS;
+    scols = CAST_WIDE_COLS;
+  } else {
+    const int tiles_j = d.n_pad / CAST_TILE;
+    i0 = (it.idx / tiles_j) * CAST_TILE;
+    j0 = (it.idx % tiles_j) * CAST_TILE;
+    tc = (threadIdx.x % (CAST_TILE / 4)) * 4;
+    tr = threadIdx.x / (CAST_TILE / 4);
+    rstep = CAST_TILE / 4;
+    srows = scols = CAST_TILE;
+  }
+  const int sr0 = trn ? j0 : i0, sc0 = trn ? i0 : j0;
+  float v[4][4];
   if (!FROM_BF16) {
+    f32x4 g4[4], m4[4];
+    if (d.vec4 && sr0 + srows <= d.rows && sc0 + scols <= d.cols) {
+      const MUON_GLOBAL float* G = gptr(d.G) + (int64_t)(sr0 + tr) * d.cols + sc0 + tc;
+      const MUON_GLOBAL float* Mp = gptr(d.M) + (int64_t)(sr0 + tr) * d.cols + sc0 + tc;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        g4[q] = __builtin_nontemporal_load(reinterpret_cast<const MUON_GLOBAL f32x4*>(G + (int64_t)rstep * q * d.cols));
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        m4[q] = __builtin_nontemporal_load(reinterpret_cast<const MUON_GLOBAL f32x4*>(Mp + (int64_t)rstep * q * d.cols));
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        g4[q] = load4_edge(gptr(d.G), d, sr0 + tr + rstep * q, sc0 + tc);
+        m4[q] = load4_edge(gptr(d.M), d, sr0 + tr + rstep * q, sc0 + tc);
+      }
+    }
+    // the norm scale: summed here from the matrix's partials when it has few
+    // (the finalisation kernel's order, so the same bits), else its result
+    float s;
     if (d.part_cnt <= NORM_FOLD_MAX) {
       __shared__ double red[kWaves];
       __shared__ float s_fold;
-      const float f = norm_scale(d, red);
+      const float f = norm_scale<true>(d, red);
       if (threadIdx.x == 0) s_fold = f;
-      __syncthreads();
+      lds_barrier();
       s = s_fold;
     } else {
       s = *d.scale;
     }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bool row_in = sr0 + tr + rstep * q < d.rows;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        v[q][k] = (row_in && sc0 + tc + k < d.cols) ? nesterov(g4[q][k], m4[q][k], beta) * s : 0.0f;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) load4_xin(d, sr0 + tr + rstep * q, sc0 + tc, v[q]);
   }
   MUON_GLOBAL uint16_t* X = gptr(d.X[0]);
-  const int tc = (threadIdx.x & 15) * 4;
-  const int tr = threadIdx.x >> 4;
-  float v[4][4];
-  if (!d.transposed) {
-    // all loads first, then all stores
-#pragma unroll
-    for (int q = 0; q < 4; ++q) load4_src<FROM_BF16>(d, i0 + tr + 16 * q, j0 + tc, beta, s, v[q]);
+  if (!trn) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       u32x2 w;
       w.x = pack_bf16x2(v[q][0], v[q][1]);
       w.y = pack_bf16x2(v[q][2], v[q][3]);
-      *reinterpret_cast<MUON_GLOBAL u32x2*>(X + (int64_t)(i0 + tr + 16 * q) * d.ld_x + j0 + tc) = w;
+      *reinterpret_cast<MUON_GLOBAL u32x2*>(X + (int64_t)(i0 + tr + rstep * q) * d.ld_x + j0 + tc) = w;
     }
   } else {
     // canonical (i, j) comes from source (j, i): stage a source tile whose
     // rows are canonical columns j0.. and columns are canonical rows i0..
 #pragma unroll
-    for (int q = 0; q < 4; ++q) load4_src<FROM_BF16>(d, j0 + tr + 16 * q, i0 + tc, beta, s, v[q]);
-#pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int k = 0; k < 4; ++k) T[tr + 16 * q][tc + k] = v[q][k];
+      for (int k = 0; k < 4; ++k) T[tr + rstep * q][tc + k] = v[q][k];
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int il = tr + 16 * q;
+      const int il = tr + rstep * q;
       u32x2 w;
       w.x = pack_bf16x2(T[tc + 0][il], T[tc + 1][il]);
       w.y = pack_bf16x2(T[tc + 2][il], T[tc + 3][il]);
