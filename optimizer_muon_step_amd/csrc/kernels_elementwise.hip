@@ -161,25 +161,38 @@ __global__ __launch_bounds__(EW_THREADS) void cast_kernel(const MatDesc* __restr
   }
 }
 
-// One work item = one CAST_TILE x CAST_TILE tile of the caller's W (items in
-// per-XCD runs of EW_TILE_RUN, as in the cast).
+// One work item = one tile of the caller's W (items in per-XCD runs of
+// EW_TILE_RUN, as in the cast): CAST_WIDE_ROWS x CAST_WIDE_COLS for an
+// untransposed matrix, CAST_TILE x CAST_TILE (X staged through LDS) for a
+// transposed one.
 __global__ __launch_bounds__(EW_THREADS) void apply_kernel(const MatDesc* __restrict__ descs,
                                                            const EwItem* __restrict__ items, float lr,
                                                            int src, int write_w) {
   __shared__ uint16_t T[CAST_TILE][CAST_TILE + 2];
   const EwItem it = items[ew_item_of_block(blockIdx.x, gridDim.x, EW_TILE_RUN)];
   const MatDesc& d = descs[it.mat];
-  const int tiles_c = (d.cols + CAST_TILE - 1) / CAST_TILE;
-  const int r0 = (it.idx / tiles_c) * CAST_TILE;
-  const int c0 = (it.idx % tiles_c) * CAST_TILE;
+  int r0, c0, tr, tc, rstep;
+  if (!d.transposed) {
+    const int tiles_c = (d.cols + CAST_WIDE_COLS - 1) / CAST_WIDE_COLS;
+    r0 = (it.idx / tiles_c) * CAST_WIDE_ROWS;
+    c0 = (it.idx % tiles_c) * CAST_WIDE_COLS;
+    tc = (threadIdx.x % (CAST_WIDE_COLS / 4)) * 4;
+    tr = threadIdx.x / (CAST_WIDE_COLS / 4);
+    rstep = CAST_WIDE_ROWS / 4;
+  } else {
+    const int tiles_c = (d.cols + CAST_TILE - 1) / CAST_TILE;
+    r0 = (it.idx / tiles_c) * CAST_TILE;
+    c0 = (it.idx % tiles_c) * CAST_TILE;
+    tc = (threadIdx.x % (CAST_TILE / 4)) * 4;
+    tr = threadIdx.x / (CAST_TILE / 4);
+    rstep = CAST_TILE / 4;
+  }
   const MUON_GLOBAL uint16_t* X = gptr(d.X[src]);
-  const int tc = (threadIdx.x & 15) * 4;
-  const int tr = threadIdx.x >> 4;
   uint32_t h[4][4];
   if (!d.transposed) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int r = min(r0 + tr + 16 * q, d.m_pad - 1);
+      const int r = min(r0 + tr + rstep * q, d.m_pad - 1);
       const u32x2 w = *reinterpret_cast<const MUON_GLOBAL u32x2*>(X + (int64_t)r * d.ld_x + c0 + tc);
       h[q][0] = w.x & 0xffffu;
       h[q][1] = w.x >> 16;
@@ -211,7 +224,7 @@ __global__ __launch_bounds__(EW_THREADS) void apply_kernel(const MatDesc* __rest
     // all loads of W first, then the stores
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int r = r0 + tr + 16 * q;
+      const int r = r0 + tr + rstep * q;
       const int64_t off = (int64_t)r * d.cols + c0 + tc;
       if (r >= d.rows) continue;
       if (vec) {
@@ -224,7 +237,7 @@ __global__ __launch_bounds__(EW_THREADS) void apply_kernel(const MatDesc* __rest
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int r = r0 + tr + 16 * q;
+      const int r = r0 + tr + rstep * q;
       const int64_t off = (int64_t)r * d.cols + c0 + tc;
       if (r >= d.rows) continue;
 #pragma unroll
@@ -242,7 +255,7 @@ __global__ __launch_bounds__(EW_THREADS) void apply_kernel(const MatDesc* __rest
     MUON_GLOBAL uint16_t* U = gptr(d.upd);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int r = r0 + tr + 16 * q;
+      const int r = r0 + tr + rstep * q;
       const int c = c0 + tc;
       if (r >= d.rows) continue;
       const int64_t off = (int64_t)r * d.cols + c;

@@ -405,7 +405,8 @@ int build_tables(int mode, const muon_shape_t* shapes, int n, char* ws_base, int
     }
     const int ct = (g.m_pad / CAST_TILE) * (g.n_pad / CAST_TILE);
     for (int t = 0; t < ct; ++t) li.cast.push_back({i, t});
-    const int at = ((g.rows + CAST_TILE - 1) / CAST_TILE) * ((g.cols + CAST_TILE - 1) / CAST_TILE);
+    const int at = g.transposed ? ((g.rows + CAST_TILE - 1) / CAST_TILE) * ((g.cols + CAST_TILE - 1) / CAST_TILE)
+                                : ((g.rows + CAST_WIDE_ROWS - 1) / CAST_WIDE_ROWS) * ((g.cols + CAST_WIDE_COLS - 1) / CAST_WIDE_COLS);
     for (int t = 0; t < at; ++t) li.apply.push_back({i, t});
   }
   // The cast re-reads what the momentum pass just streamed: walking it

@@ -69,9 +69,10 @@ constexpr int MOM_CHUNK = 16384;  // elements per momentum work item (16 float4 
 // kernel (so to the same bits); only larger matrices take that launch.
 constexpr int NORM_FOLD_MAX = 256;
 constexpr int CAST_TILE = 64;     // square tile for the cast / apply kernels
-// The cast cuts an untransposed matrix into CAST_WIDE_ROWS x CAST_WIDE_COLS
-// tiles instead (1 KB row pieces of G and M; same element count per tile, so
-// the same item count: m_pad and n_pad are multiples of both edges).
+// The cast and apply passes cut an untransposed matrix into CAST_WIDE_ROWS x
+// CAST_WIDE_COLS tiles instead (1 KB row pieces of the fp32 arrays).  The
+// cast's item count is the same for both shapes (m_pad and n_pad are
+// multiples of both edges); the apply's follows the caller's rows and cols.
 constexpr int CAST_WIDE_ROWS = 16, CAST_WIDE_COLS = 256;
 static_assert(CAST_WIDE_ROWS * CAST_WIDE_COLS == CAST_TILE * CAST_TILE, "cast tiles of equal size");
 static_assert(NS_PAD_N % CAST_WIDE_COLS == 0 && NS_PAD_M % CAST_WIDE_ROWS == 0, "wide cast tiles cover the padding");

@@ -152,7 +152,9 @@ static void check_tables(const Plan& p, const std::vector<muon_shape_t>& s, size
     CHECK((const char*)d[i].scale >= ws_lo && (const char*)(d[i].scale + 1) <= ws_lo + kControlBytes);
     mom += g.part_cnt;
     cast += (int64_t)(g.m_pad / CAST_TILE) * (g.n_pad / CAST_TILE);
-    apply += (int64_t)((g.rows + CAST_TILE - 1) / CAST_TILE) * ((g.cols + CAST_TILE - 1) / CAST_TILE);
+    apply += g.transposed ? (int64_t)((g.rows + CAST_TILE - 1) / CAST_TILE) * ((g.cols + CAST_TILE - 1) / CAST_TILE)
+                          : (int64_t)((g.rows + CAST_WIDE_ROWS - 1) / CAST_WIDE_ROWS) *
+                                ((g.cols + CAST_WIDE_COLS - 1) / CAST_WIDE_COLS);
   }
   std::sort(regions.begin(), regions.end());
   for (size_t k = 1; k < regions.size(); ++k) CHECK(regions[k].first >= regions[k - 1].second);
@@ -208,7 +210,9 @@ static void check_tables(const Plan& p, const std::vector<muon_shape_t>& s, size
       const Geometry g = geometry_of(s[it[k].mat]);
       const int lim = which == 0 ? g.part_cnt
                       : which == 1 ? (g.m_pad / CAST_TILE) * (g.n_pad / CAST_TILE)
-                                   : ((g.rows + CAST_TILE - 1) / CAST_TILE) * ((g.cols + CAST_TILE - 1) / CAST_TILE);
+                     : g.transposed ? ((g.rows + CAST_TILE - 1) / CAST_TILE) * ((g.cols + CAST_TILE - 1) / CAST_TILE)
+                                    : ((g.rows + CAST_WIDE_ROWS - 1) / CAST_WIDE_ROWS) *
+                                          ((g.cols + CAST_WIDE_COLS - 1) / CAST_WIDE_COLS);
       CHECK(it[k].idx >= 0 && it[k].idx < lim);
       CHECK(seen.insert({it[k].mat, it[k].idx}).second);
     }
