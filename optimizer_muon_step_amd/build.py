@@ -33,10 +33,12 @@ FLAGS = [
 # Per-source options on top of FLAGS.  The Gram kernel and the cast and apply
 # passes are scheduled with LLVM's iterative register-pressure-minimising
 # strategy: the same arithmetic in another instruction order (bit-identical
-# results), and same-box timings per c3 launch of Gram 89.5 against 93.1 us,
-# cast 130 against 136 and apply 145 against 148.  The other kernels keep the
-# default scheduler, which is faster for them (update 165 against 169 us,
-# momentum 167 against 277 under that strategy).
+# results), and same-box timings per c3 Gram launch of 89.5 against 93.1 us;
+# for the cast and apply passes it ties the default scheduler on c3 and c2
+# and runs the apply over 192 GPT-2-XL-shaped matrices in 2358 against
+# 2528 us.  The other kernels keep the default scheduler, which is faster for
+# them (update 165 against 169 us, momentum 167 against 277 under that
+# strategy).
 _MINREG = ["-mllvm", "-amdgpu-sched-strategy=iterative-minreg"]
 # The AdamW pass takes the iterative ILP strategy: 188.1-188.3 against
 # 190.8-190.9 us per launch on the GPT-2 AdamW set (same box), bit-identical.
