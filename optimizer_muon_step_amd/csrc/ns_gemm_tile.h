@@ -192,7 +192,9 @@ __device__ __forceinline__ void ns_gemm_tile(const MatDesc* __restrict__ descs, 
   if constexpr (PF) asm volatile("v_mov_b32 %0, 0" : "=v"(opq0));
   const int tid = threadIdx.x + opq0;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // the wave index is uniform: held in a scalar register, so the wave's
+  // tile offsets derived from it cost no vector registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wi = wave / WAVES_N, wj = wave % WAVES_N;
 
   // DMA sources.  Instruction q of this wave fills LDS slots
@@ -545,7 +547,33 @@ __device__ __forceinline__ void ns_gemm_tile(const MatDesc* __restrict__ descs, 
       }
     }
   }
-  if constexpr (PF) wait_vm_lgkm0<63>(); else wait_vm_lgkm0<0>();  // LDS only: the prefetch stays in flight
+  if constexpr (KIND == GEMM_UPDATE) {
+    // Each wave copies out the sub-tile it staged itself (its own LDS
+    // writes, complete once its LDS counter is zero), so no block barrier
+    // sits between staging and copy-out: WTN/8 16-byte pieces per row, a
+    // whole 128-byte line.  The next tile touches the staged region only
+    // after its first step's barrier.
+    if constexpr (PF) wait_vm_lgkm0<63>(); else wait_vm_lgkm0<0>();  // LDS only: the prefetch stays in flight
+    asm volatile("" ::: "memory");
+    constexpr int WCH = WTN / 8;  // 16-byte pieces per row of a wave's sub-tile
+    static_assert((WTM * WCH) % 64 == 0 && (WTM * WCH) / 64 == NSTORE, "per-wave copy-out split");
+#pragma unroll
+    for (int s = 0; s < WTM * WCH / 64; ++s) {
+      const int k = lane + 64 * s;
+      const int r = wi * WTM + k / WCH, c = wj * WCH + k % WCH;
+      const u32x4 val = *(const LDS_AS u32x4*)(E + r * ROWB + ech(r, c) * 16);
+      if (row0 + r < row_lim)
+        *reinterpret_cast<MUON_GLOBAL u32x4*>(C + (int64_t)(row0 + r) * ldc + col0 + c * 8) = val;
+    }
+    if constexpr (PF) {
+      carry.pre = has_next;
+      carry.prev_full = row0 + BM <= row_lim;
+    }
+    return;
+  }
+  // Symmetric kinds: the block copies out whole staged rows and writes the
+  // mirror, both reading other waves' staged values, so a barrier first.
+  wait_vm_lgkm0<0>();
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   constexpr int CHUNKS = BM * RCH;
@@ -560,7 +588,7 @@ __device__ __forceinline__ void ns_gemm_tile(const MatDesc* __restrict__ descs, 
         *reinterpret_cast<MUON_GLOBAL u32x4*>(C + (int64_t)(row0 + r) * ldc + col0 + c * 8) = val;
     }
   }
-  if constexpr (KIND != GEMM_UPDATE) {
+  {
     // Mirror (and the diagonal tile's lower triangle) from transposing reads
     // of the staged tile: in each 16-lane group, lane L reads row k0 + L/4,
     // columns j0 + 4 (L % 4) .. +3, and lane i receives column j0 + i, rows
@@ -596,13 +624,6 @@ __device__ __forceinline__ void ns_gemm_tile(const MatDesc* __restrict__ descs, 
       }
       *reinterpret_cast<MUON_GLOBAL u32x4*>(C + (int64_t)(col0 + j) * ldc + row0 + k0) = val;
     }
-  }
-  if constexpr (PF) {
-    // No barrier here: the next tile refills stage 1 and the parking space
-    // only after its first step's barrier, and stage 0 lies outside the
-    // staged tile.
-    carry.pre = has_next;
-    carry.prev_full = row0 + BM <= row_lim;
   }
 }
 
