@@ -54,7 +54,8 @@ __global__ __launch_bounds__(PU_NT) void poly_update_kernel(const MatDesc* __res
   const int lda = d.ld_a, ldx = d.ld_x;
   const int row0 = it.ti * UPD_ROWU;  // tile rows row0 .. row0+63 (of A, B and X)
   const int col0 = it.tj * PU_BN;     // tile columns of X
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: a scalar register
 
   // ---- DMA ----
   // A slice kt: 256 rows of 128 bytes; instruction g fills rows 8g .. 8g+7,
