@@ -30,6 +30,9 @@ hipError_t launch_gemm(int kind, const MatDesc* d, const GemmItem* items, int n_
       else if (tile == TILE_SMALL)
         ns_gemm_kernel<GEMM_UPDATE, SMALL_UPD_BM, SMALL_UPD_BN, 2, 2, SMALL_UPD_NSTAGE, UPD_ROWU, 64, false>
             <<<n_items, 256, 0, s>>>(d, items, src, ca, cb, cc, n_items, part);
+      else if (tile == TILE_SHALLOW)
+        ns_gemm_kernel<GEMM_UPDATE, SMALL_UPD_BM, SMALL_UPD_BN, 2, 2, SHALLOW_UPD_NSTAGE, UPD_ROWU, 64, false>
+            <<<n_items, 256, 0, s>>>(d, items, src, ca, cb, cc, n_items, part);
       else
         ns_gemm_kernel<GEMM_UPDATE, UPD_BM, UPD_BN, 2, 4, 2, UPD_ROWU, 64, true>
             <<<n_items < UPD_BLOCKS ? n_items : UPD_BLOCKS, 512, 0, s>>>(d, items, src, ca, cb, cc, n_items, part);

@@ -154,7 +154,8 @@ TileChoice tile_choice(const muon_shape_t* shapes, int n) {
   // A 128 x 256 tile takes about three quarters of a 192 x 256 tile's time
   // (measured 0.73-0.77), so the medium tiles win unless their extra rounds
   // over the CUs cost more than that saves.
-  if (3 * ((upd_med + NS_CUS - 1) / NS_CUS) < 4 * ((upd + NS_CUS - 1) / NS_CUS)) c.upd = TILE_MEDIUM;
+  if (3 * ((upd_med + NS_CUS - 1) / NS_CUS) < 4 * ((upd + NS_CUS - 1) / NS_CUS))
+    c.upd = upd_med < MED_UPD_MIN_TILES ? TILE_SHALLOW : TILE_MEDIUM;
   return c;
 }
 
@@ -433,8 +434,9 @@ int build_tables(int mode, const muon_shape_t* shapes, int n, char* ws_base, int
   T.gram_bm = tc.gram_bm;
   const int gram_bm = tc.gram_bm;
   const int poly_bm = tc.poly == TILE_SMALL ? SMALL_SYM : tc.poly == TILE_MEDIUM ? MED_POLY_BM : SYM_BM;
-  const int upd_bm = tc.upd == TILE_SMALL ? SMALL_UPD_BM : tc.upd == TILE_MEDIUM ? MED_UPD_BM : UPD_BM;
-  const int upd_bn = tc.upd == TILE_SMALL ? SMALL_UPD_BN : tc.upd == TILE_MEDIUM ? MED_UPD_BN : UPD_BN;
+  const bool upd_small = tc.upd == TILE_SMALL || tc.upd == TILE_SHALLOW;  // both on the small tiles
+  const int upd_bm = upd_small ? SMALL_UPD_BM : tc.upd == TILE_MEDIUM ? MED_UPD_BM : UPD_BM;
+  const int upd_bn = upd_small ? SMALL_UPD_BN : tc.upd == TILE_MEDIUM ? MED_UPD_BN : UPD_BN;
   int32_t slot = 0;
   for (int i = 0; i < n; ++i) {
     Lists& li = lists[lane_of[i]];

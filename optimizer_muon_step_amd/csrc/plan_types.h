@@ -47,10 +47,15 @@ constexpr int SMALL_SYM_NSTAGE = 8, SMALL_UPD_NSTAGE = 6;
 //           tile takes about three quarters of a large one's time).
 // Each output element accumulates its K in the same MFMA order whatever the
 // tile, so the choices change no bit, except where a Gram tile is cut.
-enum TileKind { TILE_LARGE = 0, TILE_SMALL = 1, TILE_MEDIUM = 2 };
+// A call whose medium update would have at most MED_UPD_MIN_TILES - 1 tiles
+// (leaving half the CUs or more idle) runs the update on the small tiles
+// instead, with a SHALLOW_UPD_NSTAGE ring (48 KB of LDS, several blocks per
+// CU): TILE_SHALLOW.
+enum TileKind { TILE_LARGE = 0, TILE_SMALL = 1, TILE_MEDIUM = 2, TILE_SHALLOW = 3 };
 constexpr int MED_GRAM_BM = 128;
 constexpr int MED_POLY_BM = 64, MED_POLY_NSTAGE = 4, MED_POLY_MAX_TILES = 128;
 constexpr int MED_UPD_BM = 128, MED_UPD_BN = 256;
+constexpr int MED_UPD_MIN_TILES = 129, SHALLOW_UPD_NSTAGE = 2;
 
 // A small call whose matrices all have m_pad = FUSED_M_PAD (m <= 256) runs
 // poly and update as one launch per iteration (kernels_ns_fused.hip) over

@@ -246,13 +246,15 @@ static void check_tables(const Plan& p, const std::vector<muon_shape_t>& s, size
       CHECK(t.gram_tile == (g256 < 256 ? TILE_MEDIUM : TILE_LARGE));
       CHECK(t.gram_bm == (g256 < 256 ? 128 : 256));
       CHECK(t.poly_tile == (p128 <= 128 ? TILE_MEDIUM : TILE_LARGE));
-      CHECK(t.upd_tile == (3 * ((u128 + 255) / 256) < 4 * ((u192 + 255) / 256) ? TILE_MEDIUM : TILE_LARGE));
+      const bool med = 3 * ((u128 + 255) / 256) < 4 * ((u192 + 255) / 256);
+      CHECK(t.upd_tile == (!med ? TILE_LARGE : u128 <= 128 ? TILE_SHALLOW : TILE_MEDIUM));
     }
   }
   const int gram_bm = t.gram_bm;
   const int poly_bm = t.poly_tile == TILE_SMALL ? 64 : t.poly_tile == TILE_MEDIUM ? 64 : 128;
-  const int upd_bm = t.upd_tile == TILE_SMALL ? 64 : t.upd_tile == TILE_MEDIUM ? 128 : 192;
-  const int upd_bn = t.upd_tile == TILE_SMALL ? 128 : 256;
+  const bool upd_small = t.upd_tile == TILE_SMALL || t.upd_tile == TILE_SHALLOW;
+  const int upd_bm = upd_small ? 64 : t.upd_tile == TILE_MEDIUM ? 128 : 192;
+  const int upd_bn = upd_small ? 128 : 256;
   std::map<std::tuple<int, int, int>, int64_t> ksum[3];
   auto gemm = [&](size_t off, int cnt, int kind, int lane) {
     const GemmItem* it = p.at<GemmItem>(off);
@@ -546,6 +548,12 @@ static void test_elementwise_item_map() {
 static void test_update_tile_choice() {
   const auto c5 = shapes_of({{50257, 768}, {768, 768}});
   CHECK(tile_choice(gpt2_block(1).data(), 4).upd == TILE_MEDIUM);
+  // at most 128 medium update tiles: the small tiles with the shallow ring
+  // (one 768 x 3072 matrix: 72 medium tiles; 2048 x 2048: 128; 2048 x 3072:
+  // 192 stays medium)
+  const auto k3 = shapes_of({{768, 3072}}), s2k = shapes_of({{2048, 2048}}), s23 = shapes_of({{2048, 3072}});
+  CHECK(tile_choice(k3.data(), 1).upd == TILE_SHALLOW && tile_choice(s2k.data(), 1).upd == TILE_SHALLOW);
+  CHECK(tile_choice(s23.data(), 1).upd == TILE_MEDIUM);
   CHECK(tile_choice(gpt2_block(2).data(), 8).upd == TILE_MEDIUM);
   CHECK(tile_choice(c5.data(), 2).upd == TILE_MEDIUM);
   CHECK(tile_choice(gpt2_block(4).data(), 16).upd == TILE_LARGE);

@@ -2,7 +2,7 @@
 small tiles, from the call's tile counts), but every output element
 accumulates its K in the same MFMA order whatever the tile, so a matrix's
 result does not depend on the choice unless a long-K Gram tile is cut.  The
-same matrices computed alone (medium tiles) and inside a call whose
+same matrices computed alone (medium or shallow small tiles) and inside a call whose
 companions make every kind take the large tiles agree bit for bit; no Gram
 tile is cut in either call."""
 import numpy as np
@@ -52,11 +52,12 @@ COMPANIONS = [(2048, 2048)] * 8
 @pytest.mark.parametrize("shapes", [
     # Gram 128 x 128 (36 tiles of 256: fewer than the CUs; 136 of 128, K 32
     # within twice the share of 17), poly large (136 tiles of 128), update
-    # 128 x 256 (128 tiles, 1 round, against 88 of 192 x 256, 1 round)
+    # on the small 64 x 128 tiles with the shallow ring (128 tiles of
+    # 128 x 256 would leave half the CUs idle)
     [(2048, 2048)],
-    # every kind medium: Gram 108 tiles of 128 (K 16, share 8), poly 108
-    # tiles of 128 (at most 128: 64 x 64 tiles), update 96 tiles of 128 x
-    # 256 (1 round) against 72 of 192 x 256
+    # Gram and poly medium: Gram 108 tiles of 128 (K 16, share 8), poly 108
+    # tiles of 128 (at most 128: 64 x 64 tiles); update on the shallow small
+    # tiles (96 tiles of 128 x 256 would leave most CUs idle)
     [(1024, 1024)] * 3,
 ])
 def test_medium_tiles_match_large_tiles_bit_for_bit(shapes):
